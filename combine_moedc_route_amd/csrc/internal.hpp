@@ -1,0 +1,92 @@
+// internal.hpp -- plan layout and kernel launchers shared by the host code
+// (host.cpp) and the HIP kernels (route.hip, dispatch.hip, combine.hip,
+// stub.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/moedc.h"
+
+namespace moedc {
+
+constexpr int kGroup = 128;          // quantization group (values)
+constexpr int kMaxHidden = 8192;     // 16 chunks of 512 values per wave
+constexpr int kMaxExperts = 1024;    // logical and physical
+constexpr int kMaxK = 16;            // entries per token
+constexpr int kMaxReplicas = 8;
+constexpr int kRouteTokens = 256;    // tokens per route block (one per thread)
+constexpr int64_t kSlotAlign = 512;  // dispatch slot stride granularity
+constexpr int64_t kWsAlign = 256;
+
+// Workspace byte offsets (all kWsAlign-aligned).
+struct WsLayout {
+  int64_t cap = 0;          // int32 [P]
+  int64_t capbase = 0;      // int32 [P]
+  int64_t rep_count = 0;    // int32 [E]
+  int64_t rep_table = 0;    // int32 [E][R]
+  int64_t block_counts = 0; // int32 [nblk_max][P]
+  int64_t bytes = 0;
+};
+
+struct RouteArgs {
+  const float *logits;
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *slots;
+  int32_t *dropped;
+  const int32_t *cap;
+  const int32_t *capbase;
+  const int32_t *rep_count;
+  const int32_t *rep_table;
+  int32_t *block_counts;
+  int32_t T, E, P, R, K, KR, shared, score_fn;
+};
+
+struct DispatchArgs {
+  const uint16_t *x;
+  const int32_t *slots;
+  uint8_t *dbuf;
+  int64_t slot_stride;
+  int32_t T, H, G, K;
+};
+
+struct CombineArgs {
+  const uint8_t *eout;
+  const int32_t *slots;
+  const float *w;
+  uint16_t *y;
+  int64_t eout_stride;  // bytes per slot row
+  int32_t T, H, K, fmt;
+};
+
+struct StubArgs {
+  const uint8_t *dbuf;
+  uint16_t *ebuf;
+  const int32_t *counts;
+  const int32_t *cap;
+  const int32_t *capbase;
+  int64_t slot_stride;
+  int64_t ebuf_stride;
+  int64_t total_slots;
+  int32_t H, P;
+};
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_stub(const StubArgs &a, hipStream_t s);
+
+}  // namespace moedc
+
+struct moedc_plan {
+  moedc_config cfg;                 // pointer fields point into the vectors below
+  std::vector<int32_t> cap, capbase, rep_count, rep_table;
+  int32_t K, G, nblk_max;
+  int64_t slot_stride, combine_stride, total_slots;
+  moedc::WsLayout ws;
+};

@@ -1,0 +1,231 @@
+"""Thin ctypes binding over libmoedc (argument marshalling only).
+
+Every step of route / dispatch / combine runs in the library's HIP kernels;
+this module only turns torch tensors into device pointers and the current
+HIP stream, and raises on a non-OK status.  There is no fallback: a missing
+library raises ``MoedcUnavailable``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoedc.so")
+
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = range(7)
+SCORE_SOFTMAX, SCORE_SIGMOID_NORM = 0, 1
+FMT_BF16, FMT_Q8 = 0, 1
+
+# Every symbol include/moedc.h declares.
+EXPORTS = (
+    "moedc_plan_create", "moedc_plan_destroy", "moedc_plan_sizes",
+    "moedc_plan_bind_workspace", "moedc_route", "moedc_dispatch",
+    "moedc_combine", "moedc_expert_stub", "moedc_status_string",
+    "moedc_last_hip_error",
+)
+
+
+class MoedcUnavailable(RuntimeError):
+    pass
+
+
+class MoedcError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{what}: {status_string(status)} (status {status}"
+        msg += f", hip error {hip_error})" if status == ERR_HIP else ")"
+        super().__init__(msg)
+
+
+class Config(C.Structure):
+    _fields_ = [
+        ("max_tokens", C.c_int32),
+        ("hidden", C.c_int32),
+        ("group_size", C.c_int32),
+        ("num_logical_experts", C.c_int32),
+        ("num_phys_experts", C.c_int32),
+        ("top_k", C.c_int32),
+        ("num_shared", C.c_int32),
+        ("score_fn", C.c_int32),
+        ("max_replicas", C.c_int32),
+        ("capacity", C.POINTER(C.c_int32)),
+        ("replica_table", C.POINTER(C.c_int32)),
+    ]
+
+
+class Sizes(C.Structure):
+    _fields_ = [
+        ("workspace_bytes", C.c_int64),
+        ("dispatch_buf_bytes", C.c_int64),
+        ("combine_buf_bytes", C.c_int64),
+        ("slot_stride", C.c_int64),
+        ("combine_slot_stride", C.c_int64),
+        ("total_slots", C.c_int64),
+        ("k", C.c_int32),
+        ("num_groups", C.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoedc.so from the package directory (no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoedcUnavailable(
+                f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
+                "or python combine_moedc_route_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        P, i32 = C.c_void_p, C.c_int32
+        L.moedc_plan_create.argtypes = [C.POINTER(Config), C.POINTER(C.c_void_p)]
+        L.moedc_plan_create.restype = i32
+        L.moedc_plan_destroy.argtypes = [P]
+        L.moedc_plan_destroy.restype = None
+        L.moedc_plan_sizes.argtypes = [P, C.POINTER(Sizes)]
+        L.moedc_plan_sizes.restype = i32
+        L.moedc_plan_bind_workspace.argtypes = [P, P, P]
+        L.moedc_plan_bind_workspace.restype = i32
+        L.moedc_route.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
+        L.moedc_route.restype = i32
+        L.moedc_dispatch.argtypes = [P, i32, P, P, P, P]
+        L.moedc_dispatch.restype = i32
+        L.moedc_combine.argtypes = [P, i32, P, i32, P, P, P, P]
+        L.moedc_combine.restype = i32
+        L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
+        L.moedc_expert_stub.restype = i32
+        L.moedc_status_string.argtypes = [i32]
+        L.moedc_status_string.restype = C.c_char_p
+        L.moedc_last_hip_error.argtypes = []
+        L.moedc_last_hip_error.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moedc_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise MoedcError(status, what, lib().moedc_last_hip_error() if status == ERR_HIP else 0)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a torch tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoedc takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoedc takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Plan:
+    """A validated layer description (host-only; owns no device memory)."""
+
+    def __init__(self, *, max_tokens: int, hidden: int, num_logical: int,
+                 num_phys: int, top_k: int, num_shared: int = 0,
+                 score_fn: int = SCORE_SIGMOID_NORM, capacity,
+                 replica_table=None, group_size: int = 128):
+        self._cap = np.ascontiguousarray(capacity, dtype=np.int32)
+        self._rep = (None if replica_table is None
+                     else np.ascontiguousarray(replica_table, dtype=np.int32))
+        R = 1 if self._rep is None else int(self._rep.shape[1])
+        cfg = Config(max_tokens, hidden, group_size, num_logical, num_phys, top_k,
+                     num_shared, score_fn, R,
+                     self._cap.ctypes.data_as(C.POINTER(C.c_int32)),
+                     (None if self._rep is None else
+                      self._rep.ctypes.data_as(C.POINTER(C.c_int32))))
+        h = C.c_void_p()
+        self._h = None
+        _check(lib().moedc_plan_create(C.byref(cfg), C.byref(h)), "moedc_plan_create")
+        self._h = h
+        s = Sizes()
+        _check(lib().moedc_plan_sizes(self._h, C.byref(s)), "moedc_plan_sizes")
+        self.sizes = s
+        self.max_tokens, self.hidden, self.K = max_tokens, hidden, s.k
+        self.num_logical, self.num_phys = num_logical, num_phys
+
+    @classmethod
+    def from_workload(cls, wl, max_tokens: Optional[int] = None):
+        return cls(max_tokens=wl.tokens if max_tokens is None else max_tokens,
+                   hidden=wl.hidden, num_logical=wl.num_logical,
+                   num_phys=wl.num_phys, top_k=wl.top_k, num_shared=wl.num_shared,
+                   score_fn=wl.score_fn, capacity=wl.capacity,
+                   replica_table=wl.replica_table)
+
+    def close(self):
+        if self._h is not None:
+            lib().moedc_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- device buffers (caller-owned, allocated through torch) ----------
+    def alloc(self, device="cuda"):
+        """Allocate workspace, route outputs and one dispatch/combine set."""
+        import torch
+        T, K, P = self.max_tokens, self.K, self.num_phys
+        s = self.sizes
+        u8 = dict(dtype=torch.uint8, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        bufs = dict(
+            workspace=torch.empty(max(s.workspace_bytes, 16), **u8),
+            topk_ids=torch.empty((T, K), **i32),
+            topk_w=torch.empty((T, K), dtype=torch.float32, device=device),
+            counts=torch.empty(P, **i32),
+            offsets=torch.empty(P + 1, **i32),
+            slots=torch.empty((T, K), **i32),
+            dropped=torch.empty(1, **i32),
+            dispatch_buf=torch.empty(max(s.dispatch_buf_bytes, 16), **u8),
+            combine_buf=torch.empty((max(s.total_slots, 1), self.hidden),
+                                    dtype=torch.int16, device=device),
+        )
+        self.bind_workspace(bufs["workspace"])
+        return bufs
+
+    def bind_workspace(self, ws, stream=None):
+        _check(lib().moedc_plan_bind_workspace(self._h, _ptr(ws), _stream(stream)),
+               "moedc_plan_bind_workspace")
+
+    def route(self, logits, topk_ids, topk_w, counts, offsets, slots, dropped,
+              workspace, num_tokens: Optional[int] = None, stream=None):
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moedc_route(self._h, T, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(counts), _ptr(offsets), _ptr(slots), _ptr(dropped),
+                                 _ptr(workspace), _stream(stream)), "moedc_route")
+
+    def dispatch(self, x, slots, dispatch_buf, num_tokens: Optional[int] = None,
+                 stream=None):
+        T = x.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moedc_dispatch(self._h, T, _ptr(x), _ptr(slots), _ptr(dispatch_buf),
+                                    _stream(stream)), "moedc_dispatch")
+
+    def combine(self, expert_out, fmt: int, slots, topk_w, y,
+                num_tokens: Optional[int] = None, stream=None):
+        T = y.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moedc_combine(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
+                                   _ptr(topk_w), _ptr(y), _stream(stream)), "moedc_combine")
+
+    def expert_stub(self, counts, dispatch_buf, combine_buf, workspace, stream=None):
+        _check(lib().moedc_expert_stub(self._h, _ptr(counts), _ptr(dispatch_buf),
+                                       _ptr(combine_buf), _ptr(workspace),
+                                       _stream(stream)), "moedc_expert_stub")

@@ -1,0 +1,204 @@
+/*
+ * moedc.h -- C ABI of libmoedc: MoE token routing, INT8 dispatch into static
+ * per-expert slot buffers, and gate-weighted combine, for AMD MI355X
+ * (gfx950).  Simulated expert-parallel ranks are partitions of one GPU's
+ * HBM.
+ *
+ * The three calls follow the problem statement of "CloudMatrix384:
+ * Co-Designing Supernodes for Trillion-Parameter LLM Inference", section
+ * "FusedDispatch and FusedCombine": a naive all-to-all MoE layer exchanges
+ * routing metadata, token data and expert outputs; here routing metadata
+ * becomes slot indices (moedc_route), token data is quantized to INT8 with
+ * scales and written straight into pre-allocated per-expert slots
+ * (moedc_dispatch), and expert outputs are gathered back and weighted
+ * (moedc_combine).
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device addresses owned by the caller; the
+ *    library never allocates or frees device memory and keeps no state
+ *    between calls.  Host pointers are read during the call only.
+ *  - Work is enqueued on the caller's stream and is asynchronous; no call
+ *    synchronises the stream.  A NULL stream means the default stream.
+ *  - Arguments are validated on the host before any launch; a failed
+ *    validation launches nothing.  Launch failures return MOEDC_ERR_HIP and
+ *    the HIP error code is available from moedc_last_hip_error().
+ *  - Conditions found on the device (capacity overflow) are reported only
+ *    through the `dropped` output, never through the status.
+ *  - A plan is immutable after creation; calls on one plan may run
+ *    concurrently on different streams if their buffers are disjoint.
+ *  - BF16 values are passed as uint16_t bit patterns.
+ */
+#ifndef MOEDC_H
+#define MOEDC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moedc_status {
+  MOEDC_OK = 0,
+  MOEDC_ERR_INVALID_ARG = 1,  /* NULL pointer, bad enum, inconsistent config */
+  MOEDC_ERR_SHAPE = 2,        /* token count / sizes outside the plan */
+  MOEDC_ERR_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
+  MOEDC_ERR_UNSUPPORTED = 4,  /* valid but not supported (group size, hidden > 8192, ...) */
+  MOEDC_ERR_HIP = 5,          /* a HIP launch or copy failed */
+  MOEDC_ERR_NO_MEMORY = 6     /* host allocation for the plan failed */
+} moedc_status;
+
+typedef enum moedc_score_fn {
+  /* softmax over all logical experts (gates of the picks, not renormalised) */
+  MOEDC_SCORE_SOFTMAX = 0,
+  /* logistic sigmoid of each pick, divided by the sum over the routed picks */
+  MOEDC_SCORE_SIGMOID_NORM = 1
+} moedc_score_fn;
+
+typedef enum moedc_elem_fmt {
+  MOEDC_FMT_BF16 = 0,  /* expert outputs: [total_slots][hidden] BF16 rows */
+  MOEDC_FMT_Q8 = 1     /* expert outputs in the dispatch slot layout (INT8 + scales) */
+} moedc_elem_fmt;
+
+/*
+ * Static description of one MoE layer.  Expert placement follows "Decode
+ * Phase" of the CloudMatrix384 article (routed experts, shared experts and
+ * redundant copies of popular experts, one expert per simulated rank).
+ */
+typedef struct moedc_config {
+  int32_t max_tokens;          /* largest token count any call will pass (>= 0) */
+  int32_t hidden;              /* H: multiple of 128, 128..8192 */
+  int32_t group_size;          /* quantization group; must be 128 */
+  int32_t num_logical_experts; /* E_log: logits per token, 1..1024 */
+  int32_t num_phys_experts;    /* E_phys: physical experts incl. replicas and shared, 1..1024 */
+  int32_t top_k;               /* routed picks per token, 1..E_log */
+  int32_t num_shared;          /* 0 or 1; the shared expert is physical id E_phys-1 */
+  int32_t score_fn;            /* moedc_score_fn */
+  int32_t max_replicas;        /* R: columns of replica_table, 1..8 */
+  /* Host [E_phys]: slots reserved for each physical expert (>= 0).  Their
+   * exclusive prefix sum is each expert's first slot; the sum is
+   * total_slots (< 2^31). */
+  const int32_t *capacity;
+  /* Host [E_log][R] or NULL.  Row e lists the physical ids of logical
+   * expert e's copies, then -1 padding; token t goes to copy (t mod r_e).
+   * Every routed physical id (< E_phys - num_shared) may appear once.  NULL
+   * means physical id = logical id (needs E_phys - num_shared >= E_log). */
+  const int32_t *replica_table;
+} moedc_config;
+
+typedef struct moedc_sizes {
+  int64_t workspace_bytes;      /* device workspace for route/stub (bind once) */
+  int64_t dispatch_buf_bytes;   /* total_slots * slot_stride */
+  int64_t combine_buf_bytes;    /* total_slots * combine_slot_stride */
+  int64_t slot_stride;          /* dispatch slot: round_up(H + 4*H/128, 512) bytes */
+  int64_t combine_slot_stride;  /* BF16 combine slot: 2*H bytes */
+  int64_t total_slots;          /* sum of capacities */
+  int32_t k;                    /* entries per token: top_k + num_shared */
+  int32_t num_groups;           /* H / 128 */
+} moedc_sizes;
+
+typedef struct moedc_plan moedc_plan;
+
+/* Validates *config and builds a host-only plan (copies the tables; no
+ * device memory is touched).  *out receives the plan, or NULL on error.
+ * Errors: INVALID_ARG, UNSUPPORTED, NO_MEMORY. */
+moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out);
+
+/* Frees a plan (NULL is ignored). */
+void moedc_plan_destroy(moedc_plan *plan);
+
+/* Byte sizes of the buffers the caller must allocate for this plan. */
+moedc_status moedc_plan_sizes(const moedc_plan *plan, moedc_sizes *out);
+
+/* Uploads the plan's static tables (capacities, slot bases, replica table)
+ * into the caller's device workspace of workspace_bytes (16-byte aligned),
+ * asynchronously on `stream`.  Needed once per workspace before route or
+ * the expert stand-in use it. */
+moedc_status moedc_plan_bind_workspace(const moedc_plan *plan, void *workspace,
+                                       hipStream_t stream);
+
+/*
+ * Routing.  For each of num_tokens tokens:
+ *  - picks top_k logical experts by fp32 logit, highest first, ties to the
+ *    lower id (-0 == +0), maps each to a physical copy, and computes its
+ *    gate (score_fn); a shared expert, if configured, is appended last with
+ *    weight 1.0;
+ *  - counts[p]: number of (token, entry) pairs routed to physical expert p
+ *    (before capacity); offsets[]: exclusive scan of counts, E_phys+1
+ *    entries, offsets[E_phys] = num_tokens * k;
+ *  - slots[t][j]: base(p) + rank of token t among the tokens routed to p in
+ *    ascending token order, or -1 when that rank reaches capacity[p];
+ *    *dropped: number of -1 entries.
+ * Device arrays: logits float32 [num_tokens][E_log] (16-byte aligned);
+ * topk_ids int32 [num_tokens][k] (physical ids); topk_w float32
+ * [num_tokens][k]; counts int32 [E_phys]; offsets int32 [E_phys+1]; slots
+ * int32 [num_tokens][k]; dropped int32 [1]; workspace as bound.  counts,
+ * offsets and dropped are fully rewritten on every call, also for
+ * num_tokens == 0.  Logits must be finite; otherwise picks are unspecified
+ * but always valid expert ids.
+ * Errors: INVALID_ARG, SHAPE (num_tokens outside [0, max_tokens]), ALIGN, HIP.
+ */
+moedc_status moedc_route(const moedc_plan *plan, int32_t num_tokens,
+                         const float *logits, int32_t *topk_ids, float *topk_w,
+                         int32_t *counts, int32_t *offsets, int32_t *slots,
+                         int32_t *dropped, void *workspace, hipStream_t stream);
+
+/*
+ * Dispatch: early INT8 quantization with scales, then a direct
+ * store of each token into each of its slots ("FusedDispatch and
+ * FusedCombine": quantize before sending, write into pre-allocated
+ * receiver buffers, token-granular load / quantize / write pipeline).
+ * Per token and 128-value group: amax = max |x|; scale = amax / 127 in IEEE
+ * fp32; q = clamp(round-half-even(x / scale), -127, 127) with a correctly
+ * rounded fp32 quotient (scale 0 gives q 0).  Slot s occupies bytes
+ * [s*slot_stride, (s+1)*slot_stride) of dispatch_buf: INT8 payload at
+ * [0, H), fp32 scales (little-endian) at [H, H + 4*H/128); the rest of the
+ * slot and slots no token maps to are not written.  Entries with slot -1
+ * are skipped.
+ * x: BF16 [num_tokens][H] (16-byte aligned); slots: from moedc_route;
+ * dispatch_buf: dispatch_buf_bytes (16-byte aligned).  x must be finite.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, HIP.
+ */
+moedc_status moedc_dispatch(const moedc_plan *plan, int32_t num_tokens,
+                            const uint16_t *x, const int32_t *slots,
+                            void *dispatch_buf, hipStream_t stream);
+
+/*
+ * Combine: for each token t and hidden index i,
+ *   acc = +0.0f;  acc = fmaf(topk_w[t][j], y_j[i], acc)  for j = 0..k-1
+ * skipping entries with slot -1, then y[t][i] = BF16 round-to-nearest-even
+ * of acc.  y_j is the expert output in slot slots[t][j]:
+ *  fmt BF16: expert_out is [total_slots][H] BF16 (combine_buf_bytes);
+ *  fmt Q8:   expert_out is a dispatch buffer, y_j[i] = (float)q * scale.
+ * expert_out and y (BF16 [num_tokens][H]) are 16-byte aligned.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, HIP.
+ */
+moedc_status moedc_combine(const moedc_plan *plan, int32_t num_tokens,
+                           const void *expert_out, int32_t fmt,
+                           const int32_t *slots, const float *topk_w,
+                           uint16_t *y, hipStream_t stream);
+
+/*
+ * Stand-in expert (not a step of the method; it fills combine inputs so the
+ * path can run end to end without weights).  For every occupied slot of
+ * physical expert p (the first min(counts[p], capacity[p]) slots of its
+ * window): combine_buf row = BF16( ((float)q * scale) * (1 + 0.01f*p) ),
+ * computed as two fp32 products and one fp32 sum.  Other rows are not
+ * written.  counts: from moedc_route; workspace as bound.
+ * Errors: INVALID_ARG, ALIGN, HIP.
+ */
+moedc_status moedc_expert_stub(const moedc_plan *plan, const int32_t *counts,
+                               const void *dispatch_buf, uint16_t *combine_buf,
+                               void *workspace, hipStream_t stream);
+
+/* Static English text for a status code. */
+const char *moedc_status_string(moedc_status status);
+
+/* hipError_t of the last MOEDC_ERR_HIP returned on this thread (0 if none). */
+int32_t moedc_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDC_H */

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Integer, index and byte outputs must match bit for bit;
+gates within the derived fp32 tolerance; combine output within 1 BF16 ulp
+(and is expected to be bit-identical: same operations, same order)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_moedc_route_amd import moedc as M
+from combine_moedc_route_amd import workloads as W
+
+from gpu_common import (SENTINEL, U, bf16_to_f32, check_dispatch_tokens,
+                        check_dispatch_untouched, compare_route, dev, dev_i16,
+                        gpu_dispatch, gpu_route, host_u16, log, sample_tokens,
+                        ulp_diff_bf16)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "decode", "mid", "ragged", "overflow", "replica_shared"]
+FULL = ["global", "skewed", "prefill"]
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def setup(name, tokens=None):
+    wl = W.get(name)
+    log(f"[case] {name} T={wl.tokens if tokens is None else tokens} H={wl.hidden} "
+        f"E={wl.num_logical}/{wl.num_phys} K={wl.K}")
+    x, logits = W.make_inputs(wl, tokens)
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    return wl, x, logits, plan, cfg
+
+
+# ------------------------------------------------------------------ route
+
+@pytest.mark.parametrize("name", SMALL + FULL)
+def test_route_parity(name):
+    wl, x, logits, plan, cfg = setup(name)
+    want = oracle.route(cfg, logits)
+    got, _ = gpu_route(plan, wl, logits)
+    rel = compare_route(wl, got, want)
+    log(f"  route bit-exact; max gate rel err {rel:.3g}; dropped {got['dropped']}")
+    if name in FULL:
+        assert want["dropped"] == 0
+
+
+def test_route_empty_and_ragged_token_counts():
+    wl, _, _, plan, cfg = setup("mid")
+    got, _ = gpu_route(plan, wl, np.zeros((0, wl.num_logical), np.float32))
+    assert (got["counts"] == 0).all() and (got["offsets"] == 0).all() and got["dropped"] == 0
+    for T in (1, 63, 64, 65, 255, 256, 257, 999):
+        _, logits = W.make_inputs(wl, T)
+        compare_route(wl, gpu_route(plan, wl, logits)[0], oracle.route(cfg, logits))
+
+
+@pytest.mark.parametrize("score_fn", [W.SCORE_SOFTMAX, W.SCORE_SIGMOID_NORM])
+def test_route_ties_signed_zeros_and_degenerate_rows(score_fn):
+    rng = np.random.default_rng(77)
+    T, E, K = 700, 64, 8
+    menu = np.array([-1.0, -0.0, 0.0, 0.25, 1.0, 2.0], np.float32)
+    logits = menu[rng.integers(0, len(menu), (T, E))]
+    logits[:50] = 0.0                          # all-equal rows -> ids 0..K-1
+    logits[50:100] = -0.0
+    logits[100:150, ::2] = -0.0                # +-0 mixed: equal keys
+    wl = W.Workload("ties", "", T, 128, E, E, K, 0, score_fn,
+                    np.full(E, T, np.int32), None, 0, "normal")
+    plan = M.Plan.from_workload(wl)
+    want = oracle.route(oracle.Cfg.from_workload(wl), logits)
+    compare_route(wl, gpu_route(plan, wl, logits)[0], want)
+    assert (want["topk_ids"][:150] == np.arange(K)).all()
+    # one expert, top-1
+    wl1 = W.Workload("one", "", 130, 128, 1, 1, 1, 0, score_fn,
+                     np.array([100], np.int32), None, 0, "normal")
+    lg = rng.standard_normal((130, 1)).astype(np.float32)
+    want = oracle.route(oracle.Cfg.from_workload(wl1), lg)
+    got = gpu_route(M.Plan.from_workload(wl1), wl1, lg)[0]
+    compare_route(wl1, got, want)
+    assert got["dropped"] == 30
+
+
+def test_route_deterministic():
+    wl, x, logits, plan, cfg = setup("skewed")
+    a, _ = gpu_route(plan, wl, logits)
+    b, _ = gpu_route(plan, wl, logits)
+    for k in a:
+        assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+
+
+# ------------------------------------------------------------------ dispatch
+
+@pytest.mark.parametrize("name", SMALL)
+def test_dispatch_parity(name):
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    dbuf = gpu_dispatch(plan, x, r["slots"])
+    n = check_dispatch_tokens(dbuf, x, r["slots"], np.arange(x.shape[0]), wl.hidden)
+    check_dispatch_untouched(dbuf, r["slots"], wl.hidden)
+    # Whole-buffer byte equality against the oracle's own dispatch.
+    s = plan.sizes
+    ref = np.full((s.total_slots, s.slot_stride), SENTINEL, np.uint8)
+    oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride, buf=ref)
+    assert np.array_equal(dbuf.cpu().numpy(), ref)
+    log(f"  {n} slots bit-exact")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_parity_full_size(name):
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    dbuf = gpu_dispatch(plan, x, r["slots"])
+    toks = sample_tokens(x.shape[0], 1024, 5)
+    n = check_dispatch_tokens(dbuf, x, r["slots"], toks, wl.hidden)
+    check_dispatch_untouched(dbuf, r["slots"], wl.hidden)
+    # Every kept copy of a token is byte-identical to its first copy.
+    H, G = wl.hidden, wl.hidden // 128
+    sl = torch.from_numpy(r["slots"].astype(np.int64)).cuda()
+    for t0 in range(0, x.shape[0], 4096):
+        blk = sl[t0:t0 + 4096]
+        first = dbuf[blk[:, 0], : H + 4 * G]
+        for k in range(1, wl.K):
+            keep = blk[:, k] >= 0
+            assert bool((dbuf[blk[keep, k], : H + 4 * G] == first[keep]).all())
+    # In every group with a nonzero scale some element is +-127.
+    q = dbuf[sl[:, 0], :H].view(torch.int8).view(-1, G, 128)
+    sc = dbuf[sl[:, 0], H:H + 4 * G].contiguous().view(torch.float32)
+    qmax = q.abs().amax(dim=2).to(torch.int32)
+    assert bool(((qmax == 127) | (sc == 0)).all())
+    log(f"  {n} sampled slots bit-exact; full-buffer properties hold")
+
+
+# ------------------------------------------------------------------ combine
+
+def _combine_inputs(wl, x, cfg, plan, r):
+    s = plan.sizes
+    dref = oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride)
+    ebuf = oracle.expert_stub(cfg, r["counts"], dref, s.slot_stride)
+    return dref, ebuf
+
+
+@pytest.mark.parametrize("fmt", [M.FMT_BF16, M.FMT_Q8])
+@pytest.mark.parametrize("name", SMALL)
+def test_combine_parity(name, fmt):
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    dref, ebuf = _combine_inputs(wl, x, cfg, plan, r)
+    src_host = ebuf if fmt == M.FMT_BF16 else dref
+    want = oracle.combine(cfg, src_host, fmt, r["slots"], r["topk_w"])
+    src = dev_i16(ebuf) if fmt == M.FMT_BF16 else dev(dref)
+    y = torch.full((x.shape[0], wl.hidden), -1, dtype=torch.int16, device="cuda")
+    plan.combine(src, fmt, dev(r["slots"]), dev(r["topk_w"]), y)
+    got = host_u16(y)
+    assert ulp_diff_bf16(got, want).max(initial=0) <= 1
+    assert np.array_equal(got, want), f"{(got != want).sum()} elements differ by 1 ulp"
+
+
+def test_combine_dropped_entries_and_signed_zero():
+    rng = np.random.default_rng(91)
+    T, H, K, S = 300, 640, 4, 500
+    wl = W.Workload("c", "", T, H, 8, 8, K, 0, 1, np.array([S // 8 + 1] * 7 + [S - 7 * (S // 8 + 1)],
+                    np.int32), None, 0, "normal")
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    S = plan.sizes.total_slots
+    ebuf = W.make_expert_out_bf16(92, S, H)
+    ebuf[:, ::5] = 0x8000                       # -0 values
+    ebuf[:, 1::7] ^= 0x8000
+    slots = rng.integers(0, S, (T, K)).astype(np.int32)
+    slots[rng.random((T, K)) < 0.2] = -1
+    slots[:3] = -1                              # tokens with nothing kept -> +0
+    w = W.make_gates(93, T, K)
+    w[5] = 0.0
+    want = oracle.combine(cfg, ebuf, M.FMT_BF16, slots, w)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    plan.combine(dev_i16(ebuf), M.FMT_BF16, dev(slots), dev(w), y)
+    got = host_u16(y)
+    assert np.array_equal(got, want)
+    assert (got[:3] == 0).all()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_combine_parity_full_size(name):
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    s = plan.sizes
+    T, H, K = x.shape[0], wl.hidden, wl.K
+    cbuf = torch.zeros((s.total_slots, H), dtype=torch.int16, device="cuda")
+    toks = sample_tokens(T, 512, 6)
+    rows = r["slots"][toks]                      # [n][K]
+    kept = rows[rows >= 0]
+    vals = W.make_expert_out_bf16(17, kept.size, H)
+    cbuf[torch.from_numpy(kept.astype(np.int64)).cuda()] = dev_i16(vals)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    plan.combine(cbuf, M.FMT_BF16, dev(r["slots"]), dev(r["topk_w"]), y)
+    got = host_u16(y[torch.from_numpy(toks).cuda()])
+    # Oracle on a compact buffer holding just the sampled tokens' rows.
+    compact = np.zeros((kept.size, H), np.uint16)
+    remap = np.full(rows.shape, -1, np.int32)
+    idx = 0
+    for i in range(rows.shape[0]):
+        for k in range(K):
+            if rows[i, k] >= 0:
+                compact[idx] = vals[idx]
+                remap[i, k] = idx
+                idx += 1
+    want = oracle.combine(cfg, compact, M.FMT_BF16, remap, r["topk_w"][toks])
+    assert ulp_diff_bf16(got, want).max(initial=0) <= 1
+    assert np.array_equal(got, want)
+    log(f"  {len(toks)} sampled tokens bit-exact")
+
+
+# ------------------------------------------------------------------ expert stand-in
+
+@pytest.mark.parametrize("name", ["decode", "ragged", "replica_shared", "overflow"])
+def test_expert_stub_parity(name):
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    dref, ebuf = _combine_inputs(wl, x, cfg, plan, r)
+    ws = torch.empty(plan.sizes.workspace_bytes, dtype=torch.uint8, device="cuda")
+    plan.bind_workspace(ws)
+    out = torch.zeros((plan.sizes.total_slots, wl.hidden), dtype=torch.int16, device="cuda")
+    plan.expert_stub(dev(r["counts"]), dev(dref), out, ws)
+    assert np.array_equal(host_u16(out), ebuf)
+
+
+# ------------------------------------------------------------------ end to end
+
+def _e2e(name):
+    wl, x, logits, plan, cfg = setup(name)
+    T, H, K = x.shape[0], wl.hidden, wl.K
+    b = plan.alloc()
+    lg, xd = dev(logits), dev_i16(x)
+    plan.route(lg, b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"],
+               b["dropped"], b["workspace"])
+    b["dispatch_buf"].fill_(SENTINEL)
+    plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+    identity = wl.expert == "identity"
+    if identity:
+        src, fmt = b["dispatch_buf"], M.FMT_Q8
+    else:
+        plan.expert_stub(b["counts"], b["dispatch_buf"], b["combine_buf"], b["workspace"])
+        src, fmt = b["combine_buf"], M.FMT_BF16
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    plan.combine(src, fmt, b["slots"], b["topk_w"], y)
+    torch.cuda.synchronize()
+    r = oracle.route(cfg, logits)
+    got_r = {k: b[k].cpu().numpy() for k in ("topk_ids", "topk_w", "counts", "offsets", "slots")}
+    got_r["dropped"] = int(b["dropped"].item())
+    compare_route(wl, got_r, r)
+    s = plan.sizes
+    toks = sample_tokens(T, 256, 8)
+    check_dispatch_tokens(b["dispatch_buf"].view(s.total_slots, s.slot_stride), x, r["slots"],
+                          toks, H)
+    # Final output: GPU gates differ from the oracle's by the gate tolerance,
+    # so the bound is 1 BF16 ulp + sum_k |dw_k||y_k| + 2K u sum_k |w_k y_k|.
+    dref = oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride)
+    eref = dref if identity else oracle.expert_stub(cfg, r["counts"], dref, s.slot_stride)
+    want = oracle.combine(cfg, eref, fmt, r["slots"], r["topk_w"])
+    got = host_u16(y)
+    gw = got_r["topk_w"].astype(np.float64)
+    ow = r["topk_w"].astype(np.float64)
+    for t in toks:
+        yk = np.zeros((K, H))
+        for k in range(K):
+            sl = r["slots"][t, k]
+            if sl < 0:
+                continue
+            if identity:
+                q = dref[sl, :H].view(np.int8).astype(np.float32)
+                sc = np.repeat(dref[sl, H:H + 4 * (H // 128)].view(np.float32), 128)
+                yk[k] = (q * sc).astype(np.float64)
+            else:
+                yk[k] = bf16_to_f32(eref[sl]).astype(np.float64)
+        a, bb = bf16_to_f32(got[t]).astype(np.float64), bf16_to_f32(want[t]).astype(np.float64)
+        mag = np.maximum(np.abs(a), np.abs(bb))
+        ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
+        bound = ulp + (np.abs(gw[t] - ow[t])[:, None] * np.abs(yk)).sum(0) \
+            + 2 * K * U * (np.abs(ow[t])[:, None] * np.abs(yk)).sum(0)
+        assert (np.abs(a - bb) <= bound).all(), t
+    return wl
+
+
+@pytest.mark.parametrize("name", SMALL + ["global"])
+def test_end_to_end(name):
+    _e2e(name)
