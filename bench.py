@@ -1,0 +1,321 @@
+"""Benchmark of the MoE route -> INT8 dispatch -> combine path on one MI355X.
+
+One step = moedc_route + moedc_dispatch + moedc_combine over the 30720-token
+global decode batch (hidden 7168, 256 experts, top-8, INT8 groups of 128,
+capacity 1920 per expert, BF16 expert outputs), alternating two static
+dispatch/combine buffer sets.  The stand-in expert fills both combine sets
+once before timing; it is not part of the path and is not timed.
+
+Prints ONE JSON line.  Per-kernel durations come from HIP events recorded
+on the stream the library launches on (torch's current stream).
+
+Extra modes (measurement plumbing, not the product path):
+  --calib-copy            time a plain device copy of known size (the
+                          reference kernel for scaling rocprofv3 byte counters)
+  --summarize-rocprof DIR write a text summary of rocprofv3 CSV output
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = ("dispatch+combine µs and tokens/s at 30720×7168 top-8/256; "
+          "% of HBM peak GB/s")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = {
+    "combine": "combine_moedc_route_amd/csrc/combine.hip",
+    "dispatch": "combine_moedc_route_amd/csrc/dispatch.hip",
+    "route": "combine_moedc_route_amd/csrc/route.hip",
+}
+
+
+def algorithmic_bytes(T, H, K, E):
+    """Bytes the method must move (padding, unoccupied slots excluded)."""
+    G = H // 128
+    return dict(
+        route=4 * T * E + 12 * T * K,
+        dispatch=2 * T * H + 4 * T * K + T * K * (H + 4 * G),
+        combine=2 * T * K * H + 8 * T * K + 2 * T * H,
+        combine_q8=T * K * (H + 4 * G) + 8 * T * K + 2 * T * H,
+    )
+
+
+def source_sha(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from committed PMC runs, or None if the kernel
+    source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(tokens=16384):
+    """The oracle, single-threaded, on a bounded sample of the same workload:
+    `tokens` tokens drawn with the same recipe and seed, per-expert capacity
+    scaled to 2x their mean load.  Times route + dispatch + combine (the stand-in expert is untimed,
+    as on the GPU)."""
+    import numpy as np
+
+    import oracle
+    from combine_moedc_route_amd import workloads as W
+    wl = W.get("global")
+    cap = 2 * tokens * wl.K // wl.num_phys
+    sub = W.Workload("global-prefix", "", tokens, wl.hidden, wl.num_logical, wl.num_phys,
+                     wl.top_k, 0, wl.score_fn, np.full(wl.num_phys, cap, np.int32), None,
+                     wl.seed, wl.logits_kind)
+    x, logits = W.make_inputs(sub)
+    cfg = oracle.Cfg.from_workload(sub)
+    H, G = wl.hidden, wl.hidden // 128
+    sd = -(-(H + 4 * G) // 512) * 512
+    S = cap * wl.num_phys
+    t0 = time.perf_counter()
+    r = oracle.route(cfg, logits)
+    t1 = time.perf_counter()
+    dbuf = oracle.dispatch(cfg, x, r["slots"], S, sd)
+    t2 = time.perf_counter()
+    ebuf = oracle.expert_stub(cfg, r["counts"], dbuf, sd)
+    t3 = time.perf_counter()
+    oracle.combine(cfg, ebuf, oracle.FMT_BF16, r["slots"], r["topk_w"])
+    t4 = time.perf_counter()
+    sec = (t1 - t0) + (t2 - t1) + (t4 - t3)
+    return {"value": tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{tokens} tokens of the 30720-token workload recipe, capacity {cap}/expert; "
+                      f"route {1e3 * (t1 - t0):.1f} ms, dispatch {1e3 * (t2 - t1):.1f} ms, "
+                      f"combine {1e3 * (t4 - t3):.1f} ms (single thread)"}
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+
+    wl = W.get(args.workload)
+    T, H, K, E = wl.tokens, wl.hidden, wl.K, wl.num_logical
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    plan = M.Plan.from_workload(wl)
+    s = plan.sizes
+    x, logits = W.make_inputs(wl)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    lg = torch.from_numpy(logits).to(dev)
+    del x, logits
+    ws = torch.empty(s.workspace_bytes, dtype=torch.uint8, device=dev)
+    plan.bind_workspace(ws)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids = torch.empty((T, K), **i32)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(wl.num_phys, **i32)
+    offsets = torch.empty(wl.num_phys + 1, **i32)
+    slots = torch.empty((T, K), **i32)
+    dropped = torch.empty(1, **i32)
+    sets = []
+    for _ in range(2):  # double-buffered static dispatch/combine buffers
+        sets.append((torch.empty(s.dispatch_buf_bytes, dtype=torch.uint8, device=dev),
+                     torch.empty((s.total_slots, H), dtype=torch.int16, device=dev)))
+    y = torch.empty((T, H), dtype=torch.int16, device=dev)
+    fmt = M.FMT_Q8 if args.combine_fmt == "q8" else M.FMT_BF16
+
+    def route():
+        plan.route(lg, ids, w, counts, offsets, slots, dropped, ws)
+
+    for dbuf, cbuf in sets:  # fill combine inputs once (untimed)
+        route()
+        plan.dispatch(xd, slots, dbuf)
+        plan.expert_stub(counts, dbuf, cbuf, ws)
+    torch.cuda.synchronize()
+    assert int(dropped.item()) == 0
+
+    def step(i, ev=None):
+        dbuf, cbuf = sets[i & 1]
+        src = dbuf if fmt == M.FMT_Q8 else cbuf
+        if ev:
+            ev[0].record()
+        route()
+        if ev:
+            ev[1].record()
+        plan.dispatch(xd, slots, dbuf)
+        if ev:
+            ev[2].record()
+        plan.combine(src, fmt, slots, w, y)
+        if ev:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    r_us = [1e3 * e[0].elapsed_time(e[1]) for e in evs]
+    d_us = [1e3 * e[1].elapsed_time(e[2]) for e in evs]
+    c_us = [1e3 * e[2].elapsed_time(e[3]) for e in evs]
+    mean = statistics.fmean
+    ab = algorithmic_bytes(T, H, K, E)
+    cb = ab["combine_q8"] if fmt == M.FMT_Q8 else ab["combine"]
+    dc_us = mean(d_us) + mean(c_us)
+    comb_gbps = cb / (mean(c_us) * 1e-6) / 1e9
+    disp_gbps = ab["dispatch"] / (mean(d_us) * 1e-6) / 1e9
+    dc_gbps = (ab["dispatch"] + cb) / (dc_us * 1e-6) / 1e9
+    # Dominant kernel: the one with the larger mean duration.
+    dom = "combine" if mean(c_us) >= mean(d_us) else "dispatch"
+    dom_bytes, dom_gbps = (cb, comb_gbps) if dom == "combine" else (ab["dispatch"], disp_gbps)
+    traffic = measured_traffic(dom) if fmt == M.FMT_BF16 else None
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "tokens": T, "hidden": H, "experts": wl.num_phys, "top_k": K,
+            "group": 128, "capacity_per_expert": int(wl.capacity[0]),
+            "combine_input": "bf16" if fmt == M.FMT_BF16 else "q8",
+            "step": "route + dispatch + combine, buffer sets alternating",
+        },
+        "route_us": mean(r_us),
+        "dispatch_us": mean(d_us),
+        "combine_us": mean(c_us),
+        "dispatch_us_median": statistics.median(d_us),
+        "combine_us_median": statistics.median(c_us),
+        "dispatch_plus_combine_us": dc_us,
+        "dispatch_plus_combine_tokens_per_s": T / (dc_us * 1e-6),
+        "dispatch_GBps": disp_gbps,
+        "combine_GBps": comb_gbps,
+        "dispatch_plus_combine_GBps": dc_gbps,
+        "dispatch_plus_combine_frac_of_hbm_peak": dc_gbps / HBM_PEAK_GBPS,
+        "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": cb, "route": ab["route"]},
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": dom_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": dom_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def calib_copy(args):
+    """A plain device-to-device copy of a known byte count (reads N, writes N)."""
+    import torch
+    n = args.calib_bytes
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    print(json.dumps({"calib_copy_bytes": n, "us_per_copy": us,
+                      "GBps_read_plus_write": 2 * n / (us * 1e-6) / 1e9}), flush=True)
+
+
+def summarize_rocprof(d, out):
+    """Condense rocprofv3 CSV output (kernel stats and/or counters) to text."""
+    import csv
+    lines = []
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"# kernel stats: {os.path.relpath(path, d)}")
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        lines.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel")
+        for r in rows:
+            lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                         f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                         f"{float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        lines.append(f"# counters: {os.path.relpath(path, d)}")
+        agg = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "")[:110], r.get("Counter_Name", ""))
+                agg.setdefault(key, []).append(float(r.get("Counter_Value", "nan")))
+        lines.append(f"{'n':>5} {'mean_per_dispatch':>20} {'counter':>14}  kernel")
+        for (k, c), v in sorted(agg.items()):
+            lines.append(f"{len(v):5d} {statistics.fmean(v):20.1f} {c:>14}  {k}")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="global")
+    ap.add_argument("--combine-fmt", choices=["bf16", "q8"], default="bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--calib-bytes", type=int, default=4 << 30)
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--out")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.out)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (the MoE path's simulated "
+              "expert-parallel ranks are partitions of one GPU's HBM); --gpus must be 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy(args)
+        return
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

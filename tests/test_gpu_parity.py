@@ -74,7 +74,7 @@ def test_route_ties_signed_zeros_and_degenerate_rows(score_fn):
     plan = M.Plan.from_workload(wl)
     want = oracle.route(oracle.Cfg.from_workload(wl), logits)
     compare_route(wl, gpu_route(plan, wl, logits)[0], want)
-    assert (want["topk_ids"][:150] == np.arange(K)).all()
+    assert (want["topk_ids"][:100] == np.arange(K)).all()
     # one expert, top-1
     wl1 = W.Workload("one", "", 130, 128, 1, 1, 1, 0, score_fn,
                      np.array([100], np.int32), None, 0, "normal")
