@@ -289,6 +289,44 @@ def summarize_rocprof(d, out):
     print(text)
 
 
+def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+    """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE runs,
+    each counter scaled by what it reads for a plain copy of known size."""
+    import csv
+
+    def per_kernel(d, counter):
+        agg = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        agg.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.fmean(v) * 1024 for k, v in agg.items()}  # KiB -> B
+
+    def copy_factor(d, counter):
+        v = [b for k, b in per_kernel(d, counter).items() if "copyBuffer" in k]
+        return copy_bytes / max(v)
+
+    ff = copy_factor(copy_fetch_dir, "FETCH_SIZE")
+    fw = copy_factor(copy_write_dir, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
+                     f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
+                     f"{copy_bytes}-byte copy); valid while source_sha matches."}
+    for key, tag in (("combine", "combine_kernel<8, false>"), ("dispatch", "dispatch_kernel<14>"),
+                     ("route", "route_topk_rank<8, false>")):
+        kf = [k for k in fetch if tag in k]
+        kw = [k for k in write if tag in k]
+        if not kf or not kw:
+            continue
+        out[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]),
+                    "fetch_bytes": fetch[kf[0]] * ff, "write_bytes": write[kw[0]] * fw,
+                    "bytes_per_launch": fetch[kf[0]] * ff + write[kw[0]] * fw}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,8 +339,13 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=4 << 30)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--record-traffic", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--out")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, copy_bytes=args.calib_bytes)
+        return
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.out)
         return

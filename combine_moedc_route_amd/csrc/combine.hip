@@ -7,10 +7,15 @@
 // acc = +0; acc = fma(w_j, y_j, acc) over the token's entries in route
 // order, dropped entries skipped; BF16 round-to-nearest-even at the end.
 //
-// Mapping: one wave64 per token; per 512-value chunk every lane issues the
-// K independent 16-byte (BF16) or 8-byte (INT8) gathers before the FMA
-// chain, so K * 1 KiB per wave is in flight.  A dropped entry loads nothing
-// and contributes fma(0, 0, acc) = acc, which leaves acc bit-identical.
+// Mapping: one wave64 per token.  The token's H values are covered in
+// groups of kChunks 512-value chunks (lane l holds values 512c + 8l .. +8
+// of chunk c).  Within a group the wave walks the K expert rows in route
+// order and, for each row, issues the loads of all kChunks chunks back to
+// back: a contiguous 7 KiB (BF16) run of one row instead of 1 KiB pieces of
+// K rows in turn, which keeps HBM row-buffer locality on a gather whose rows
+// are scattered over the slot buffer.  Expert rows and the output are
+// touched once, so loads and stores carry the non-temporal hint.  A dropped
+// entry loads nothing and contributes fma(0, 0, acc) = acc exactly.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -21,53 +26,26 @@ namespace moedc {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kChunks = 7;  // 512-value chunks per group: 7168 = 2 groups
 
-template <int K>
-__global__ __launch_bounds__(256) void combine_bf16_kernel(CombineArgs a) {
-  const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int H = a.H;
-  int slot[K];
-  float w[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    slot[k] = uniform(a.slots[t * K + k]);
-    w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
-  }
-  uint4 *yrow = reinterpret_cast<uint4 *>(a.y + t * H);
-  const int nch = (H + 511) / 512;
-#pragma unroll 2
-  for (int c = 0; c < nch; ++c) {
-    const int e = c * 512 + lane * 8;
-    if (e >= H) continue;
-    uint4 v[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      v[k] = make_uint4(0, 0, 0, 0);
-      if (slot[k] >= 0)
-        v[k] = *reinterpret_cast<const uint4 *>(a.eout + (int64_t)slot[k] * a.eout_stride +
-                                                 (int64_t)e * 2);
-    }
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(w[k], bf16_lo(d[i]), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(w[k], bf16_hi(d[i]), acc[2 * i + 1]);
-      }
-    }
-    yrow[c * 64 + lane] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-  }
+__device__ __forceinline__ uint4 load_nt16(const uint8_t *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int K>
-__global__ __launch_bounds__(256) void combine_q8_kernel(CombineArgs a) {
+__device__ __forceinline__ uint2 load_nt8(const uint8_t *p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ void store_nt16(uint16_t *p, const float (&acc)[8]) {
+  const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(p));
+}
+
+template <int K, bool Q8>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int lane = lane_id();
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
   if (t >= a.T) return;
@@ -79,39 +57,63 @@ __global__ __launch_bounds__(256) void combine_q8_kernel(CombineArgs a) {
     slot[k] = uniform(a.slots[t * K + k]);
     w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
   }
-  uint4 *yrow = reinterpret_cast<uint4 *>(a.y + t * H);
+  uint16_t *yrow = a.y + t * H;
   const int nch = (H + 511) / 512;
-#pragma unroll 2
-  for (int c = 0; c < nch; ++c) {
-    const int e = c * 512 + lane * 8;
-    if (e >= H) continue;
-    uint2 v[K];
-    float sc[K];
+  for (int g0 = 0; g0 < nch; g0 += kChunks) {
+    float acc[kChunks][8];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      v[k] = make_uint2(0, 0);
-      sc[k] = 0.0f;
-      if (slot[k] >= 0) {
-        const uint8_t *row = a.eout + (int64_t)slot[k] * a.eout_stride;
-        v[k] = *reinterpret_cast<const uint2 *>(row + e);
-        sc[k] = *reinterpret_cast<const float *>(row + H + 4 * (e >> 7));
+      const uint8_t *row = a.eout + (int64_t)(slot[k] < 0 ? 0 : slot[k]) * a.eout_stride;
+      if (!Q8) {
+        uint4 v[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const int e = (g0 + c) * 512 + lane * 8;
+          v[c] = make_uint4(0, 0, 0, 0);
+          if (slot[k] >= 0 && e < H) v[c] = load_nt16(row + (int64_t)e * 2);
+        }
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const uint32_t d[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[c][2 * i] = __builtin_fmaf(w[k], bf16_lo(d[i]), acc[c][2 * i]);
+            acc[c][2 * i + 1] = __builtin_fmaf(w[k], bf16_hi(d[i]), acc[c][2 * i + 1]);
+          }
+        }
+      } else {
+        uint2 v[kChunks];
+        float sc[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const int e = (g0 + c) * 512 + lane * 8;
+          v[c] = make_uint2(0, 0);
+          sc[c] = 0.0f;
+          if (slot[k] >= 0 && e < H) {
+            v[c] = load_nt8(row + e);
+            sc[c] = *reinterpret_cast<const float *>(row + H + 4 * (e >> 7));
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const uint32_t d[2] = {v[c].x, v[c].y};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int qi = (int)(int8_t)((d[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+            acc[c][i] = __builtin_fmaf(w[k], (float)qi * sc[c], acc[c][i]);
+          }
+        }
       }
     }
-    float acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint32_t d[2] = {v[k].x, v[k].y};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int qi = (int)(int8_t)((d[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-        const float dq = (float)qi * sc[k];
-        acc[i] = __builtin_fmaf(w[k], dq, acc[i]);
-      }
+    for (int c = 0; c < kChunks; ++c) {
+      const int e = (g0 + c) * 512 + lane * 8;
+      if (e < H) store_nt16(yrow + e, acc[c]);
     }
-    yrow[c * 64 + lane] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
 }
 
@@ -125,9 +127,9 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
 #define MOEDC_CASE(k)                                                  \
   case k:                                                              \
     if (q8)                                                            \
-      combine_q8_kernel<k><<<grid, 256, 0, s>>>(a);                    \
+      combine_kernel<k, true><<<grid, 256, 0, s>>>(a);                 \
     else                                                               \
-      combine_bf16_kernel<k><<<grid, 256, 0, s>>>(a);                  \
+      combine_kernel<k, false><<<grid, 256, 0, s>>>(a);                \
     break;
     MOEDC_CASE(1) MOEDC_CASE(2) MOEDC_CASE(3) MOEDC_CASE(4) MOEDC_CASE(5) MOEDC_CASE(6)
     MOEDC_CASE(7) MOEDC_CASE(8) MOEDC_CASE(9) MOEDC_CASE(10) MOEDC_CASE(11) MOEDC_CASE(12)

@@ -12,12 +12,14 @@
 // ceil(H/512) chunks; in chunk c lane l holds values [512c + 8l, +8) from
 // one 16-byte load, so a 16-lane DPP row holds exactly one 128-value group.
 // amax is a DPP row max over the BF16 magnitudes (bit patterns, no float
-// compare needed), the scale is one IEEE fp32 division per group and each
-// value is quantized with a correctly rounded fp32 quotient.  The wave then
+// compare needed), the scale is one IEEE fp32 division per group, and each
+// value's quotient x/scale is the correctly rounded fp32 quotient, obtained
+// from one IEEE reciprocal per group plus an fma correction.  The wave then
 // writes the token's payload (8 bytes per lane, 512 contiguous bytes per
 // store instruction) and its scales (one dword per lane) into each of the
-// K slots.  Many waves per CU overlap one token's loads with other tokens'
-// quantize and store phases.
+// K slots, with the non-temporal hint (slots are written once and read by
+// a later kernel).  Many waves per CU overlap one token's loads with other
+// tokens' quantize and store phases.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -38,15 +40,46 @@ __device__ __forceinline__ uint32_t absmax8(const uint4 &v) {
   return m;
 }
 
-__device__ __forceinline__ uint32_t q8(float x, float s) {
-  // s > 0 here.  IEEE quotient, round half to even, symmetric clamp.
-  const float r = fminf(fmaxf(rintf(x / s), -127.0f), 127.0f);
-  return (uint32_t)((int)r) & 0xFFu;
+__device__ __forceinline__ uint32_t clamp_q(float r) {
+  return (uint32_t)((int)fminf(fmaxf(r, -127.0f), 127.0f)) & 0xFFu;
 }
 
-__device__ __forceinline__ uint32_t q8x4(uint32_t d0, uint32_t d1, float s) {
-  return q8(bf16_lo(d0), s) | (q8(bf16_hi(d0), s) << 8) | (q8(bf16_lo(d1), s) << 16) |
-         (q8(bf16_hi(d1), s) << 24);
+// q = clamp(rne(x / s)) with the IEEE quotient computed by the compiler's
+// correctly rounded division.  Used when 1/s would not be a normal number.
+__device__ __forceinline__ uint32_t q8_div(float x, float s) { return clamp_q(rintf(x / s)); }
+
+// Same result with one division per group: y = RN(1/s) (IEEE), q0 = RN(x*y),
+// r = x - q0*s (exact in one fma), q1 = RN(q0 + r*y).  By Markstein's
+// correction theorem q1 = RN(x/s) whenever y is the correctly rounded
+// reciprocal and nothing under- or overflows, which holds for s >= 2^-100
+// (the device test checks every BF16 (x, amax) pair).
+__device__ __forceinline__ uint32_t q8_rcp(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, s, x);
+  return clamp_q(rintf(__builtin_fmaf(r, y, q0)));
+}
+
+__device__ __forceinline__ uint2 quant8(const uint4 &v, float s) {
+  uint32_t b[8];
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  if (s >= 0x1p-100f) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[2 * i] = q8_rcp(bf16_lo(d[i]), s, y);
+      b[2 * i + 1] = q8_rcp(bf16_hi(d[i]), s, y);
+    }
+  } else if (s > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[2 * i] = q8_div(bf16_lo(d[i]), s);
+      b[2 * i + 1] = q8_div(bf16_hi(d[i]), s);
+    }
+  } else {
+    return make_uint2(0, 0);  // all-zero group: scale 0, codes 0
+  }
+  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
 }
 
 template <int NCH>
@@ -70,12 +103,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   for (int c = 0; c < NCH; ++c) {
     const uint32_t m = row16_max_u32(absmax8(v[c]));
     const float s = __uint_as_float(m << 16) / 127.0f;
-    if (s > 0.0f) {
-      q[c].x = q8x4(v[c].x, v[c].y, s);
-      q[c].y = q8x4(v[c].z, v[c].w, s);
-    } else {
-      q[c] = make_uint2(0, 0);
-    }
+    q[c] = quant8(v[c], s);
     // Group 4c + r lives in DPP row r; lane 4c + r collects its scale.
     const float sg = __shfl(s, (lane & 3) * 16);
     if ((lane >> 2) == c) my_scale = sg;
@@ -89,9 +117,12 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int e = c * 512 + lane * 8;
-      if (e < H) *reinterpret_cast<uint2 *>(dst + e) = q[c];
+      if (e < H) {
+        const u32x2 qq = {q[c].x, q[c].y};
+        __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
+      }
     }
-    if (lane < a.G) *reinterpret_cast<float *>(dst + H + 4 * lane) = my_scale;
+    if (lane < a.G) __builtin_nontemporal_store(my_scale, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 

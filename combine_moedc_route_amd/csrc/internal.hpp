@@ -17,7 +17,7 @@ constexpr int kMaxHidden = 8192;     // 16 chunks of 512 values per wave
 constexpr int kMaxExperts = 1024;    // logical and physical
 constexpr int kMaxK = 16;            // entries per token
 constexpr int kMaxReplicas = 8;
-constexpr int kRouteTokens = 256;    // tokens per route block (one per thread)
+constexpr int kRouteTokens = 64;     // tokens per route block (4 lanes per token)
 constexpr int64_t kSlotAlign = 512;  // dispatch slot stride granularity
 constexpr int64_t kWsAlign = 256;
 

@@ -30,9 +30,10 @@ namespace moedc {
 
 namespace {
 
-constexpr int kTileE = 32;                 // experts per LDS tile
-constexpr int kWaves = kRouteTokens / 64;  // waves per route block
+constexpr int kSub = 4;                    // lanes per token in the top-k scan
+constexpr int kTileE = 64;                 // experts per LDS tile (16 per lane)
 constexpr int kIdBits = 11;                // ids 0..1024 (1024 = inactive lane)
+static_assert(kRouteTokens * kSub == 256, "one token per lane of wave 0");
 
 // Insert (v, e) into a list kept in descending value order; equal values
 // keep the earlier (lower-id) entry first because ids arrive ascending.
@@ -49,147 +50,217 @@ __device__ __forceinline__ void topk_insert(float (&val)[KR], int (&id)[KR], flo
   }
 }
 
+// Stage logits[row0 .. row0+kRouteTokens)[e0 .. e0+ec) into the LDS tile,
+// all loads of a thread issued before its LDS stores.
+__device__ __forceinline__ void load_tile(float (&tile)[kRouteTokens][kTileE + 1],
+                                          const RouteArgs &a, int64_t row0, int e0, int ec,
+                                          bool vec4) {
+  const int tid = threadIdx.x;
+  if (vec4) {  // E % 4 == 0: rows are 16-byte aligned, ec is a multiple of 4
+    constexpr int kPer = kRouteTokens * kTileE / 4 / 256;
+    float4 v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row0 + r < a.T && c < ec)
+        v[j] = *reinterpret_cast<const float4 *>(a.logits + (row0 + r) * a.E + e0 + c);
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
+      tile[r][c] = v[j].x;
+      tile[r][c + 1] = v[j].y;
+      tile[r][c + 2] = v[j].z;
+      tile[r][c + 3] = v[j].w;
+    }
+  } else {
+    constexpr int kPer = kRouteTokens * kTileE / 256;
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int f = tid + 256 * j, r = f / kTileE, c = f % kTileE;
+      v[j] = 0.f;
+      if (row0 + r < a.T && c < ec) v[j] = a.logits[(row0 + r) * a.E + e0 + c];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int f = tid + 256 * j;
+      tile[f / kTileE][f % kTileE] = v[j];
+    }
+  }
+}
+
+// One block = kRouteTokens tokens x kSub lanes.  Lane `sub` of token r scans
+// columns [16 sub, 16 sub + 16) of every 64-expert tile and keeps a local
+// top-KR; wave 0 (lane = token) merges the four lists, computes gates and the
+// physical ids, and ranks the block's entries with bit-sliced ballots.
 template <int KR, bool SHARED>
-__global__ __launch_bounds__(kRouteTokens) void route_topk_rank(RouteArgs a) {
+__global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   constexpr int KT = KR + (SHARED ? 1 : 0);
   __shared__ float tile[kRouteTokens][kTileE + 1];
-  __shared__ int32_t hist[kWaves][kMaxExperts];
+  __shared__ float lval[kRouteTokens][kSub][KR];
+  __shared__ int lid[kRouteTokens][kSub][KR];
+  __shared__ float zpart[kRouteTokens][kSub];
+  __shared__ float mrow[kRouteTokens];
+  __shared__ int32_t hist[kMaxExperts];
   __shared__ int32_t ids_lds[KT][kRouteTokens];
-  __shared__ int32_t rank_lds[KT][kRouteTokens];
 
   const int tid = threadIdx.x;
-  const int wave = uniform(tid >> 6);
+  const int r = tid >> 2, sub = tid & 3;
   const int64_t row0 = (int64_t)blockIdx.x * kRouteTokens;
-  const int64_t t = row0 + tid;
-  const bool active = t < a.T;
   const int E = a.E, P = a.P;
+  const bool vec4 = (E & 3) == 0;
 
-  for (int i = tid; i < kWaves * P; i += kRouteTokens) hist[i / P][i % P] = 0;
+  for (int i = tid; i < P; i += 256) hist[i] = 0;
 
-  // ---- top-k over tiles of kTileE experts ------------------------------
+  // ---- scan: local top-KR over this lane's columns ----------------------
   float val[KR];
   int id[KR];
 #pragma unroll
   for (int j = 0; j < KR; ++j) {
     val[j] = -__builtin_inff();
-    id[j] = j;  // valid distinct ids even if a row has no finite logit
+    id[j] = j;  // valid ids even if a row has no finite logit
   }
   for (int e0 = 0; e0 < E; e0 += kTileE) {
     const int ec = min(kTileE, E - e0);
     __syncthreads();
-    for (int f = tid; f < kRouteTokens * kTileE; f += kRouteTokens) {
-      const int r = f / kTileE, c = f % kTileE;
-      float v = -__builtin_inff();
-      if (row0 + r < a.T && c < ec) v = a.logits[(row0 + r) * E + e0 + c];
-      tile[r][c] = v;
-    }
+    load_tile(tile, a, row0, e0, ec, vec4);
     __syncthreads();
-    for (int c = 0; c < ec; ++c) topk_insert<KR>(val, id, tile[tid][c], e0 + c);
+    const int c1 = min(16 * sub + 16, ec);
+    for (int c = 16 * sub; c < c1; ++c) topk_insert<KR>(val, id, tile[r][c], e0 + c);
+  }
+#pragma unroll
+  for (int j = 0; j < KR; ++j) {
+    lval[r][sub][j] = val[j];
+    lid[r][sub][j] = id[j];
+  }
+  __syncthreads();
+
+  // ---- wave 0: merge the four lists (value desc, id asc) -----------------
+  const int64_t t = row0 + tid;
+  const bool active = tid < kRouteTokens && t < a.T;
+  if (tid < kRouteTokens) {
+    int h[kSub] = {0, 0, 0, 0};  // next unread entry of each lane's list
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      float bv = -__builtin_inff();
+      int bi = 0, bs = -1;
+#pragma unroll
+      for (int s2 = 0; s2 < kSub; ++s2) {
+        if (h[s2] < KR) {
+          const float v = lval[tid][s2][h[s2]];
+          const int i = lid[tid][s2][h[s2]];
+          if (bs < 0 || v > bv || (v == bv && i < bi)) {
+            bv = v;
+            bi = i;
+            bs = s2;
+          }
+        }
+      }
+      val[j] = bv;
+      id[j] = bi;
+#pragma unroll
+      for (int s2 = 0; s2 < kSub; ++s2) h[s2] += bs == s2;
+    }
+    mrow[tid] = val[0];
   }
 
-  // ---- gates -------------------------------------------------------------
-  float w[KT];
+  // ---- softmax denominator: second pass over the tiles ---------------------
+  float Z = 0.0f;
   if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
-    const float m = val[0];
-    float Z = 0.0f;
+    __syncthreads();
+    const float m = mrow[r];
+    float z = 0.0f;
     for (int e0 = 0; e0 < E; e0 += kTileE) {
       const int ec = min(kTileE, E - e0);
       __syncthreads();
-      for (int f = tid; f < kRouteTokens * kTileE; f += kRouteTokens) {
-        const int r = f / kTileE, c = f % kTileE;
-        float v = -__builtin_inff();
-        if (row0 + r < a.T && c < ec) v = a.logits[(row0 + r) * E + e0 + c];
-        tile[r][c] = v;
-      }
+      load_tile(tile, a, row0, e0, ec, vec4);
       __syncthreads();
-      for (int c = 0; c < ec; ++c) Z += expf(tile[tid][c] - m);
+      const int c1 = min(16 * sub + 16, ec);
+      for (int c = 16 * sub; c < c1; ++c) z += expf(tile[r][c] - m);
     }
+    zpart[r][sub] = z;
+    __syncthreads();
+    if (tid < kRouteTokens) Z = ((zpart[tid][0] + zpart[tid][1]) + zpart[tid][2]) + zpart[tid][3];
+  }
+
+  // ---- wave 0: gates, physical ids, outputs ---------------------------------
+  int pk[KT];
+  if (tid < kRouteTokens) {
+    float w[KT];
+    if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
 #pragma unroll
-    for (int j = 0; j < KR; ++j) w[j] = expf(val[j] - m) / Z;
-  } else {
-    float s[KR];
-    float S = 0.0f;
+      for (int j = 0; j < KR; ++j) w[j] = expf(val[j] - val[0]) / Z;
+    } else {
+      float sg[KR];
+      float S = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        sg[j] = 1.0f / (1.0f + expf(-val[j]));
+        S += sg[j];
+      }
+#pragma unroll
+      for (int j = 0; j < KR; ++j) w[j] = sg[j] / S;
+    }
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
-      s[j] = 1.0f / (1.0f + expf(-val[j]));
-      S += s[j];
+      const int e = id[j];
+      pk[j] = a.rep_table[e * a.R + (int)t % a.rep_count[e]];
+    }
+    if (SHARED) {
+      pk[KT - 1] = P - 1;
+      w[KT - 1] = 1.0f;
+    }
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        a.topk_ids[t * KT + j] = pk[j];
+        a.topk_w[t * KT + j] = w[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KT; ++j) pk[j] = kMaxExperts;  // matches no real id
     }
 #pragma unroll
-    for (int j = 0; j < KR; ++j) w[j] = s[j] / S;
+    for (int j = 0; j < KT; ++j) ids_lds[j][tid] = pk[j];
   }
+  __syncthreads();
 
-  // ---- physical mapping ----------------------------------------------------
-  int pk[KT];
-#pragma unroll
-  for (int j = 0; j < KR; ++j) {
-    const int e = id[j];
-    const int r = a.rep_count[e];
-    pk[j] = a.rep_table[e * a.R + (int)t % r];
-  }
-  if (SHARED) {
-    pk[KT - 1] = P - 1;
-    w[KT - 1] = 1.0f;
-  }
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < KT; ++j) {
-      a.topk_ids[t * KT + j] = pk[j];
-      a.topk_w[t * KT + j] = w[j];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KT; ++j) pk[j] = kMaxExperts;  // matches no real id
-  }
-
-  // ---- in-wave ranks: bit-sliced ballots ------------------------------------
+  // ---- wave 0: ranks from bit-sliced ballots --------------------------------
   // For entry (lane, j) with id v, the lanes whose entry j2 also holds v are
   // AND over id bits b of (bit b of v ? ballot(bit b) : ~ballot(bit b)) -- a
   // match-any built from ballots.  A token holds an id at most once, so the
   // rank of the lane for v is the number of lower lanes holding v at any
-  // position, and the lane with rank 0 is the wave's leader for v.
-#pragma unroll
-  for (int j = 0; j < KT; ++j) ids_lds[j][tid] = pk[j];
-  __syncthreads();  // ids staged; hist zeroed; tiles consumed
-  const uint64_t act = __ballot(active);
-  const uint64_t lt = lanemask_lt();
-#pragma unroll 1
-  for (int j = 0; j < KT; ++j) {
-    const int v = ids_lds[j][tid];
-    int rank = 0, cnt = 0;
-#pragma unroll 1
-    for (int j2 = 0; j2 < KT; ++j2) {
-      const int other = ids_lds[j2][tid];
-      uint64_t m = act;
-#pragma unroll
-      for (int b = 0; b < kIdBits; ++b) {
-        const uint64_t B = __ballot((other >> b) & 1);
-        m &= ((v >> b) & 1) ? B : ~B;
-      }
-      rank += __popcll(m & lt);
-      cnt += __popcll(m);
-    }
-    rank_lds[j][tid] = rank;
-    if (active && rank == 0) hist[wave][v] = cnt;
-  }
-  __syncthreads();
-
-  // ---- in-block ranks via per-wave counts in LDS ----------------------------
-  if (active) {
+  // position; the lane with rank 0 writes the block's count for v.
+  if (tid < kRouteTokens) {
+    const uint64_t act = __ballot(active);
+    const uint64_t lt = lanemask_lt();
 #pragma unroll 1
     for (int j = 0; j < KT; ++j) {
       const int v = ids_lds[j][tid];
-      int base = 0;
-      for (int w2 = 0; w2 < wave; ++w2) base += hist[w2][v];
-      a.slots[t * KT + j] = base + rank_lds[j][tid];  // finished by route_slots
+      int rank = 0, cnt = 0;
+#pragma unroll 1
+      for (int j2 = 0; j2 < KT; ++j2) {
+        const int other = ids_lds[j2][tid];
+        uint64_t m = act;
+#pragma unroll
+        for (int b = 0; b < kIdBits; ++b) {
+          const uint64_t B = __ballot((other >> b) & 1);
+          m &= ((v >> b) & 1) ? B : ~B;
+        }
+        rank += __popcll(m & lt);
+        cnt += __popcll(m);
+      }
+      if (active) {
+        a.slots[t * KT + j] = rank;  // block-local rank, finished by route_slots
+        if (rank == 0) hist[v] = cnt;
+      }
     }
   }
+  __syncthreads();
   int32_t *bc = a.block_counts + (int64_t)blockIdx.x * P;
-  for (int p = tid; p < P; p += kRouteTokens) {
-    int c = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) c += hist[w2][p];
-    bc[p] = c;
-  }
+  for (int p = tid; p < P; p += 256) bc[p] = hist[p];
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
@@ -209,12 +280,20 @@ __global__ __launch_bounds__(256) void route_block_scan(int32_t *bc, int32_t *co
   if (p >= P) return;
   const int l = lane_id();
   int carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 64) {
-    const int b = b0 + l;
-    const int v = b < nblk ? bc[(int64_t)b * P + p] : 0;
-    const int incl = wave_inclusive_scan(v);
-    if (b < nblk) bc[(int64_t)b * P + p] = carry + incl - v;
-    carry += __shfl(incl, 63);
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + 64 * u + l;
+      v[u] = b < nblk ? bc[(int64_t)b * P + p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = b0 + 64 * u + l;
+      const int incl = wave_inclusive_scan(v[u]);
+      if (b < nblk) bc[(int64_t)b * P + p] = carry + incl - v[u];
+      carry += __shfl(incl, 63);
+    }
   }
   if (l == 0) counts[p] = carry;
 }
@@ -269,9 +348,9 @@ __global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries)
 template <int KR>
 hipError_t launch_topk(const RouteArgs &a, int nblk, hipStream_t s) {
   if (a.shared)
-    route_topk_rank<KR, true><<<nblk, kRouteTokens, 0, s>>>(a);
+    route_topk_rank<KR, true><<<nblk, 256, 0, s>>>(a);
   else
-    route_topk_rank<KR, false><<<nblk, kRouteTokens, 0, s>>>(a);
+    route_topk_rank<KR, false><<<nblk, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -82,30 +82,35 @@ def lib():
             raise MoedcUnavailable(
                 f"{LIB_PATH} is missing; build it with __graft_entry__.build() "
                 "or python combine_moedc_route_amd/build.py")
-        L = C.CDLL(LIB_PATH)
-        P, i32 = C.c_void_p, C.c_int32
-        L.moedc_plan_create.argtypes = [C.POINTER(Config), C.POINTER(C.c_void_p)]
-        L.moedc_plan_create.restype = i32
-        L.moedc_plan_destroy.argtypes = [P]
-        L.moedc_plan_destroy.restype = None
-        L.moedc_plan_sizes.argtypes = [P, C.POINTER(Sizes)]
-        L.moedc_plan_sizes.restype = i32
-        L.moedc_plan_bind_workspace.argtypes = [P, P, P]
-        L.moedc_plan_bind_workspace.restype = i32
-        L.moedc_route.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
-        L.moedc_route.restype = i32
-        L.moedc_dispatch.argtypes = [P, i32, P, P, P, P]
-        L.moedc_dispatch.restype = i32
-        L.moedc_combine.argtypes = [P, i32, P, i32, P, P, P, P]
-        L.moedc_combine.restype = i32
-        L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
-        L.moedc_expert_stub.restype = i32
-        L.moedc_status_string.argtypes = [i32]
-        L.moedc_status_string.restype = C.c_char_p
-        L.moedc_last_hip_error.argtypes = []
-        L.moedc_last_hip_error.restype = i32
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path):
+    """dlopen a libmoedc build and declare its C signatures."""
+    L = C.CDLL(path)
+    P, i32 = C.c_void_p, C.c_int32
+    L.moedc_plan_create.argtypes = [C.POINTER(Config), C.POINTER(C.c_void_p)]
+    L.moedc_plan_create.restype = i32
+    L.moedc_plan_destroy.argtypes = [P]
+    L.moedc_plan_destroy.restype = None
+    L.moedc_plan_sizes.argtypes = [P, C.POINTER(Sizes)]
+    L.moedc_plan_sizes.restype = i32
+    L.moedc_plan_bind_workspace.argtypes = [P, P, P]
+    L.moedc_plan_bind_workspace.restype = i32
+    L.moedc_route.argtypes = [P, i32, P, P, P, P, P, P, P, P, P]
+    L.moedc_route.restype = i32
+    L.moedc_dispatch.argtypes = [P, i32, P, P, P, P]
+    L.moedc_dispatch.restype = i32
+    L.moedc_combine.argtypes = [P, i32, P, i32, P, P, P, P]
+    L.moedc_combine.restype = i32
+    L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
+    L.moedc_expert_stub.restype = i32
+    L.moedc_status_string.argtypes = [i32]
+    L.moedc_status_string.restype = C.c_char_p
+    L.moedc_last_hip_error.argtypes = []
+    L.moedc_last_hip_error.restype = i32
+    return L
 
 
 def status_string(status: int) -> str:
