@@ -9,11 +9,11 @@
 // expert's static base plus the rank of t among that expert's tokens in
 // ascending token order, so the layout is deterministic without atomics:
 //
-//   K1 route_topk_rank  one thread per token: top-k over LDS tiles of the
-//                       logits, gates, replica mapping; in-wave ranks from
-//                       bit-sliced ballots (a match-any over expert ids),
-//                       in-block ranks from an LDS table of per-wave counts;
-//                       writes per-block expert counts.
+//   K1 route_topk_rank  64 tokens x 4 lanes per block: top-k over LDS tiles
+//                       of the logits (next tile prefetched into registers),
+//                       4-way merge, gates, replica mapping; block-local
+//                       ranks and counts from per-expert 64-bit token masks
+//                       in LDS (popcounts); writes per-block expert counts.
 //   K2 route_block_scan one wave per expert: exclusive scan over blocks of
 //                       the per-block counts (DPP/shuffle wave scan); the
 //                       total is counts[p].
@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kSub = 4;                    // lanes per token in the top-k scan
 constexpr int kTileE = 64;                 // experts per LDS tile (16 per lane)
-constexpr int kIdBits = 11;                // ids 0..1024 (1024 = inactive lane)
 static_assert(kRouteTokens * kSub == 256, "one token per lane of wave 0");
 
 // Insert (v, e) into a list kept in descending value order; equal values
@@ -50,43 +49,51 @@ __device__ __forceinline__ void topk_insert(float (&val)[KR], int (&id)[KR], flo
   }
 }
 
-// Stage logits[row0 .. row0+kRouteTokens)[e0 .. e0+ec) into the LDS tile,
-// all loads of a thread issued before its LDS stores.
-__device__ __forceinline__ void load_tile(float (&tile)[kRouteTokens][kTileE + 1],
-                                          const RouteArgs &a, int64_t row0, int e0, int ec,
-                                          bool vec4) {
+// A thread's share of one 64-expert tile of the block's logits, held in
+// registers so the next tile's loads are in flight while this one is scanned.
+struct TileRegs {
+  float v[kRouteTokens * kTileE / 256];
+};
+
+__device__ __forceinline__ void tile_fetch(TileRegs &tr, const RouteArgs &a, int64_t row0,
+                                           int e0, int ec, bool vec4) {
   const int tid = threadIdx.x;
-  if (vec4) {  // E % 4 == 0: rows are 16-byte aligned, ec is a multiple of 4
-    constexpr int kPer = kRouteTokens * kTileE / 4 / 256;
-    float4 v[kPer];
+  if (vec4) {  // E % 4 == 0: rows are 16-byte aligned and ec is a multiple of 4
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
-      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (row0 + r < a.T && c < ec)
-        v[j] = *reinterpret_cast<const float4 *>(a.logits + (row0 + r) * a.E + e0 + c);
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
-      tile[r][c] = v[j].x;
-      tile[r][c + 1] = v[j].y;
-      tile[r][c + 2] = v[j].z;
-      tile[r][c + 3] = v[j].w;
+        x = *reinterpret_cast<const float4 *>(a.logits + (row0 + r) * a.E + e0 + c);
+      tr.v[4 * j] = x.x;
+      tr.v[4 * j + 1] = x.y;
+      tr.v[4 * j + 2] = x.z;
+      tr.v[4 * j + 3] = x.w;
     }
   } else {
-    constexpr int kPer = kRouteTokens * kTileE / 256;
-    float v[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < 16; ++j) {
       const int f = tid + 256 * j, r = f / kTileE, c = f % kTileE;
-      v[j] = 0.f;
-      if (row0 + r < a.T && c < ec) v[j] = a.logits[(row0 + r) * a.E + e0 + c];
+      tr.v[j] = (row0 + r < a.T && c < ec) ? a.logits[(row0 + r) * a.E + e0 + c] : 0.f;
     }
+  }
+}
+
+__device__ __forceinline__ void tile_store(float (&tile)[kRouteTokens][kTileE + 1],
+                                           const TileRegs &tr, bool vec4) {
+  const int tid = threadIdx.x;
+  if (vec4) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tile[r][c + i] = tr.v[4 * j + i];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
       const int f = tid + 256 * j;
-      tile[f / kTileE][f % kTileE] = v[j];
+      tile[f / kTileE][f % kTileE] = tr.v[j];
     }
   }
 }
@@ -94,7 +101,11 @@ __device__ __forceinline__ void load_tile(float (&tile)[kRouteTokens][kTileE + 1
 // One block = kRouteTokens tokens x kSub lanes.  Lane `sub` of token r scans
 // columns [16 sub, 16 sub + 16) of every 64-expert tile and keeps a local
 // top-KR; wave 0 (lane = token) merges the four lists, computes gates and the
-// physical ids, and ranks the block's entries with bit-sliced ballots.
+// physical ids.  Ranks come from one 64-bit token mask per expert in LDS:
+// bit l of mask[p] is set iff token l of the block routes to p (atomic OR,
+// so the result does not depend on arrival order); a token's rank for p is
+// the popcount of the mask below its bit, the block's count the full
+// popcount.
 template <int KR, bool SHARED>
 __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   constexpr int KT = KR + (SHARED ? 1 : 0);
@@ -103,8 +114,7 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   __shared__ int lid[kRouteTokens][kSub][KR];
   __shared__ float zpart[kRouteTokens][kSub];
   __shared__ float mrow[kRouteTokens];
-  __shared__ int32_t hist[kMaxExperts];
-  __shared__ int32_t ids_lds[KT][kRouteTokens];
+  __shared__ unsigned long long tokmask[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int r = tid >> 2, sub = tid & 3;
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   const int E = a.E, P = a.P;
   const bool vec4 = (E & 3) == 0;
 
-  for (int i = tid; i < P; i += 256) hist[i] = 0;
+  for (int i = tid; i < P; i += 256) tokmask[i] = 0ull;
 
   // ---- scan: local top-KR over this lane's columns ----------------------
   float val[KR];
@@ -122,11 +132,14 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
     val[j] = -__builtin_inff();
     id[j] = j;  // valid ids even if a row has no finite logit
   }
+  TileRegs tr;
+  tile_fetch(tr, a, row0, 0, min(kTileE, E), vec4);
   for (int e0 = 0; e0 < E; e0 += kTileE) {
     const int ec = min(kTileE, E - e0);
     __syncthreads();
-    load_tile(tile, a, row0, e0, ec, vec4);
+    tile_store(tile, tr, vec4);
     __syncthreads();
+    if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
     const int c1 = min(16 * sub + 16, ec);
     for (int c = 16 * sub; c < c1; ++c) topk_insert<KR>(val, id, tile[r][c], e0 + c);
   }
@@ -172,11 +185,13 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
     __syncthreads();
     const float m = mrow[r];
     float z = 0.0f;
+    tile_fetch(tr, a, row0, 0, min(kTileE, E), vec4);
     for (int e0 = 0; e0 < E; e0 += kTileE) {
       const int ec = min(kTileE, E - e0);
       __syncthreads();
-      load_tile(tile, a, row0, e0, ec, vec4);
+      tile_store(tile, tr, vec4);
       __syncthreads();
+      if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
       const int c1 = min(16 * sub + 16, ec);
       for (int c = 16 * sub; c < c1; ++c) z += expf(tile[r][c] - m);
     }
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
     if (tid < kRouteTokens) Z = ((zpart[tid][0] + zpart[tid][1]) + zpart[tid][2]) + zpart[tid][3];
   }
 
-  // ---- wave 0: gates, physical ids, outputs ---------------------------------
+  // ---- wave 0: gates, physical ids, outputs, token masks --------------------
   int pk[KT];
   if (tid < kRouteTokens) {
     float w[KT];
@@ -217,50 +232,19 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
       for (int j = 0; j < KT; ++j) {
         a.topk_ids[t * KT + j] = pk[j];
         a.topk_w[t * KT + j] = w[j];
+        atomicOr(&tokmask[pk[j]], 1ull << tid);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KT; ++j) pk[j] = kMaxExperts;  // matches no real id
     }
-#pragma unroll
-    for (int j = 0; j < KT; ++j) ids_lds[j][tid] = pk[j];
   }
   __syncthreads();
-
-  // ---- wave 0: ranks from bit-sliced ballots --------------------------------
-  // For entry (lane, j) with id v, the lanes whose entry j2 also holds v are
-  // AND over id bits b of (bit b of v ? ballot(bit b) : ~ballot(bit b)) -- a
-  // match-any built from ballots.  A token holds an id at most once, so the
-  // rank of the lane for v is the number of lower lanes holding v at any
-  // position; the lane with rank 0 writes the block's count for v.
-  if (tid < kRouteTokens) {
-    const uint64_t act = __ballot(active);
+  if (active) {
     const uint64_t lt = lanemask_lt();
-#pragma unroll 1
-    for (int j = 0; j < KT; ++j) {
-      const int v = ids_lds[j][tid];
-      int rank = 0, cnt = 0;
-#pragma unroll 1
-      for (int j2 = 0; j2 < KT; ++j2) {
-        const int other = ids_lds[j2][tid];
-        uint64_t m = act;
 #pragma unroll
-        for (int b = 0; b < kIdBits; ++b) {
-          const uint64_t B = __ballot((other >> b) & 1);
-          m &= ((v >> b) & 1) ? B : ~B;
-        }
-        rank += __popcll(m & lt);
-        cnt += __popcll(m);
-      }
-      if (active) {
-        a.slots[t * KT + j] = rank;  // block-local rank, finished by route_slots
-        if (rank == 0) hist[v] = cnt;
-      }
-    }
+    for (int j = 0; j < KT; ++j)  // block-local rank, finished by route_slots
+      a.slots[t * KT + j] = __popcll(tokmask[pk[j]] & lt);
   }
-  __syncthreads();
   int32_t *bc = a.block_counts + (int64_t)blockIdx.x * P;
-  for (int p = tid; p < P; p += 256) bc[p] = hist[p];
+  for (int p = tid; p < P; p += 256) bc[p] = __popcll(tokmask[p]);
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
