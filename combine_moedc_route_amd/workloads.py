@@ -46,6 +46,7 @@ class Workload:
     outliers: Optional[tuple] = None        # ("per_group", group, rows, factor) | ("fraction", frac, factor)
     expert: str = "stub"                    # "identity" (combine reads dispatch slots) | "stub"
     zipf_s: float = 1.1
+    group_size: int = 128                   # values per fp32 scale: 128, or hidden (per token)
 
     @property
     def K(self) -> int:
@@ -96,6 +97,10 @@ def _make_all():
         "decode", "96 tokens (one die's decode batch), hidden 7168, 256 experts, "
         "top-8 sigmoid-normalised", 96, 7168, 256, 256, 8, 0, SCORE_SIGMOID_NORM,
         _uniform_caps(256, 96), None, 2, "normal")
+    w["decode_pt"] = dataclasses.replace(
+        w["decode"], name="decode_pt", description="96 tokens, hidden 7168, 256 experts, "
+        "top-8 sigmoid-normalised, one INT8 scale per token", seed=6, group_size=7168,
+        outliers=("per_group", 96, 8, 50.0))
     w["global"] = Workload(
         "global", "30720 tokens (global decode batch), hidden 7168, 256 experts, "
         "top-8 from U[0,1) logits, capacity 1920 per expert", 30720, 7168, 256,

@@ -25,6 +25,7 @@ _lib = None
 class OrcCfg(C.Structure):
     _fields_ = [
         ("hidden", C.c_int32),
+        ("group_size", C.c_int32),
         ("num_logical", C.c_int32),
         ("num_phys", C.c_int32),
         ("top_k", C.c_int32),
@@ -54,7 +55,7 @@ def lib():
         L.orc_f32_to_bf16_array.restype = None
         L.orc_route.argtypes = [C.POINTER(OrcCfg), i32, P, P, P, P, P, P, P]
         L.orc_quantize_group.argtypes = [i32, P, P, P]
-        L.orc_quantize_token.argtypes = [i32, P, P, P]
+        L.orc_quantize_token.argtypes = [i32, i32, P, P, P]
         L.orc_dispatch.argtypes = [C.POINTER(OrcCfg), i32, P, P, P, i64]
         L.orc_expert_stub.argtypes = [C.POINTER(OrcCfg), P, P, i64, P, i64]
         L.orc_combine.argtypes = [C.POINTER(OrcCfg), i32, P, i32, i64, P, P, P]
@@ -75,24 +76,26 @@ class Cfg:
     """Holds the numpy arrays a ``OrcCfg`` points into, keeping them alive."""
 
     def __init__(self, hidden, num_logical, num_phys, top_k, num_shared,
-                 score_fn, capacity, replica_table=None):
+                 score_fn, capacity, replica_table=None, group_size=128):
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.replica_table = (None if replica_table is None else
                               np.ascontiguousarray(replica_table, dtype=np.int32))
         R = 1 if self.replica_table is None else self.replica_table.shape[1]
         self.c = OrcCfg(
-            hidden, num_logical, num_phys, top_k, num_shared, score_fn, R,
+            hidden, group_size, num_logical, num_phys, top_k, num_shared, score_fn, R,
             (None if self.replica_table is None else
              self.replica_table.ctypes.data_as(C.POINTER(C.c_int32))),
             self.capacity.ctypes.data_as(C.POINTER(C.c_int32)))
         self.hidden = hidden
+        self.group_size = group_size
         self.num_phys = num_phys
         self.K = top_k + num_shared
 
     @classmethod
     def from_workload(cls, wl):
         return cls(wl.hidden, wl.num_logical, wl.num_phys, wl.top_k,
-                   wl.num_shared, wl.score_fn, wl.capacity, wl.replica_table)
+                   wl.num_shared, wl.score_fn, wl.capacity, wl.replica_table,
+                   getattr(wl, "group_size", 128))
 
     def check(self):
         return lib().orc_check_cfg(C.byref(self.c))
@@ -137,14 +140,15 @@ def quantize_group(x_bits):
     return q, s[0]
 
 
-def quantize_tokens(x_bits):
-    """Quantize rows of a [T][H] uint16 BF16 array -> (q [T][H] int8, s [T][H/128] f32)."""
+def quantize_tokens(x_bits, group_size=128):
+    """Quantize rows of a [T][H] uint16 BF16 array in groups of group_size
+    -> (q [T][H] int8, s [T][H/group_size] f32)."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     T, H = x.shape
     q = np.empty((T, H), np.int8)
-    s = np.empty((T, H // 128), np.float32)
+    s = np.empty((T, H // group_size), np.float32)
     for t in range(T):
-        _check(lib().orc_quantize_token(H, _p(x[t]), _p(q[t]), _p(s[t])),
+        _check(lib().orc_quantize_token(H, group_size, _p(x[t]), _p(q[t]), _p(s[t])),
                "quantize_token")
     return q, s
 

@@ -18,7 +18,9 @@
  *  R2  gates: softmax over all logical experts (not renormalised) or the
  *      logistic sigmoid of each pick normalised over the picks; computed in
  *      fp64 and rounded once to fp32.  A shared expert takes weight 1.
- *  R3  INT8 granularity: one fp32 scale per 128 consecutive hidden values;
+ *  R3  INT8 granularity: one fp32 scale per group of consecutive hidden
+ *      values, the group being 128 values or the whole token ("INT8
+ *      Quantization": activation scales are per token and dynamic);
  *      scale = amax/127 in fp32, q = clamp(round-half-even(x/scale), +-127);
  *      an all-zero group has scale 0 and q = 0.
  *  R4  slot layout: within each physical expert, occupied slots hold tokens
@@ -90,6 +92,7 @@ static int32_t replica_id(const orc_cfg *c, int32_t e, int32_t copy) {
 int orc_check_cfg(const orc_cfg *c) {
   if (!c || !c->capacity) return ORC_EINVAL;
   if (c->hidden <= 0 || c->hidden % 128 != 0) return ORC_EINVAL;
+  if (c->group_size != 128 && c->group_size != c->hidden) return ORC_EINVAL;
   if (c->num_logical <= 0 || c->top_k <= 0 || c->top_k > c->num_logical) return ORC_EINVAL;
   if (c->top_k > 64) return ORC_EINVAL;
   if (c->num_shared != 0 && c->num_shared != 1) return ORC_EINVAL;
@@ -249,10 +252,10 @@ int orc_quantize_group(int32_t n, const uint16_t *x, int8_t *q, float *scale) {
   return ORC_OK;
 }
 
-int orc_quantize_token(int32_t H, const uint16_t *x, int8_t *q, float *scales) {
-  if (H <= 0 || H % 128) return ORC_EINVAL;
-  for (int32_t g = 0; g < H / 128; ++g) {
-    int rc = orc_quantize_group(128, x + 128 * g, q + 128 * g, scales + g);
+int orc_quantize_token(int32_t H, int32_t gs, const uint16_t *x, int8_t *q, float *scales) {
+  if (H <= 0 || gs <= 0 || H % gs) return ORC_EINVAL;
+  for (int32_t g = 0; g < H / gs; ++g) {
+    int rc = orc_quantize_group(gs, x + (int64_t)gs * g, q + (int64_t)gs * g, scales + g);
     if (rc) return rc;
   }
   return ORC_OK;
@@ -262,13 +265,14 @@ int orc_dispatch(const orc_cfg *c, int32_t T, const uint16_t *x,
                  const int32_t *slots, uint8_t *dbuf, int64_t slot_stride) {
   int rc = orc_check_cfg(c);
   if (rc) return rc;
-  const int32_t H = c->hidden, G = H / 128, K = c->top_k + c->num_shared;
+  const int32_t H = c->hidden, gs = c->group_size, G = H / gs;
+  const int32_t K = c->top_k + c->num_shared;
   if (slot_stride < (int64_t)H + 4 * G) return ORC_EINVAL;
   int8_t *q = malloc((size_t)H);
   float *s = malloc(sizeof(float) * (size_t)G);
   if (!q || !s) { free(q); free(s); return ORC_EINVAL; }
   for (int32_t t = 0; t < T && rc == ORC_OK; ++t) {
-    rc = orc_quantize_token(H, x + (int64_t)t * H, q, s);
+    rc = orc_quantize_token(H, gs, x + (int64_t)t * H, q, s);
     for (int32_t j = 0; j < K && rc == ORC_OK; ++j) {
       int32_t slot = slots[(int64_t)t * K + j];
       if (slot < 0) continue;
@@ -289,7 +293,7 @@ int orc_expert_stub(const orc_cfg *c, const int32_t *counts,
                     uint16_t *ebuf, int64_t ebuf_stride) {
   int rc = orc_check_cfg(c);
   if (rc) return rc;
-  const int32_t H = c->hidden;
+  const int32_t H = c->hidden, gs = c->group_size;
   int64_t base = 0;
   for (int32_t p = 0; p < c->num_phys; ++p) {
     float m = 1.0f + 0.01f * (float)p;  /* two roundings: product, then sum */
@@ -299,7 +303,7 @@ int orc_expert_stub(const orc_cfg *c, const int32_t *counts,
       uint16_t *dst = (uint16_t *)((uint8_t *)ebuf + (base + j) * ebuf_stride);
       for (int32_t i = 0; i < H; ++i) {
         float s;
-        memcpy(&s, src + H + 4 * (i / 128), sizeof s);
+        memcpy(&s, src + H + 4 * (i / gs), sizeof s);
         float dq = (float)(int8_t)src[i] * s;
         dst[i] = orc_f32_to_bf16(dq * m);
       }
@@ -317,7 +321,7 @@ int orc_combine(const orc_cfg *c, int32_t T, const void *eout, int32_t fmt,
   int rc = orc_check_cfg(c);
   if (rc) return rc;
   if (fmt != ORC_FMT_BF16 && fmt != ORC_FMT_Q8) return ORC_EINVAL;
-  const int32_t H = c->hidden, K = c->top_k + c->num_shared;
+  const int32_t H = c->hidden, gs = c->group_size, K = c->top_k + c->num_shared;
   const uint8_t *E = (const uint8_t *)eout;
   for (int32_t t = 0; t < T; ++t) {
     for (int32_t i = 0; i < H; ++i) {
@@ -333,7 +337,7 @@ int orc_combine(const orc_cfg *c, int32_t T, const void *eout, int32_t fmt,
           v = bf16_to_f32(b);
         } else {
           float s;
-          memcpy(&s, row + H + 4 * (i / 128), sizeof s);
+          memcpy(&s, row + H + 4 * (i / gs), sizeof s);
           v = (float)(int8_t)row[i] * s;
         }
         acc = fmaf(topk_w[(int64_t)t * K + j], v, acc);

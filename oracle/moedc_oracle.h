@@ -43,6 +43,7 @@ enum {
 
 typedef struct orc_cfg {
   int32_t hidden;         /* H, a multiple of 128 */
+  int32_t group_size;     /* values per fp32 scale: 128, or H (one scale per token) */
   int32_t num_logical;    /* logical routed experts the router scores */
   int32_t num_phys;       /* physical expert instances (replicas + shared included) */
   int32_t top_k;          /* routed picks per token */
@@ -72,11 +73,11 @@ int orc_route(const orc_cfg *c, int32_t T, const float *logits,
 /* Quantize n BF16 values (one group) to INT8 with one fp32 scale. */
 int orc_quantize_group(int32_t n, const uint16_t *x, int8_t *q, float *scale);
 
-/* Quantize one token of H values: H/128 groups -> q[H], scales[H/128]. */
-int orc_quantize_token(int32_t H, const uint16_t *x, int8_t *q, float *scales);
+/* Quantize one token of H values in groups of gs: q[H], scales[H/gs]. */
+int orc_quantize_token(int32_t H, int32_t gs, const uint16_t *x, int8_t *q, float *scales);
 
 /* Dispatch T tokens into a host slot buffer of the given byte stride:
- * payload at byte 0, fp32 scales at byte H.  Bytes past H + 4*(H/128) of
+ * payload at byte 0, fp32 scales at byte H.  Bytes past H + 4*(H/gs) of
  * each slot and unoccupied slots are not written. */
 int orc_dispatch(const orc_cfg *c, int32_t T, const uint16_t *x,
                  const int32_t *slots, uint8_t *dbuf, int64_t slot_stride);

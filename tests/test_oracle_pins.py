@@ -416,3 +416,46 @@ def test_expert_stub_closed_form(orc):
             s = np.repeat(row[H:H + 4 * (H // 128)].view(np.float32), 128)
             want = f32_bits_to_bf16_torch((q * s) * m)
             assert (eb[base[p] + j] == want).all()
+
+
+# ---------------------------------------------------------------- per-token scale
+
+def test_page_facts_per_token_slot():
+    f = facts()
+    H = f["hidden"]
+    assert H + 4 <= f["int8_token_kb_with_scale"] * 1024      # 7172 B
+    assert -(-(H + 4) // 512) * 512 == 7680
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_quantizer_per_token_against_numpy(orc, seed):
+    wl = W.get("decode_pt")
+    x, _ = W.make_inputs(wl, 96)
+    rng = np.random.default_rng(seed)
+    x = x[rng.permutation(96)]
+    x[3] = 0                                   # all-zero token
+    x[4, :] = 0
+    x[4, 17] = 0x0001                          # one subnormal element only
+    q, s = orc.quantize_tokens(x, group_size=wl.hidden)
+    qn, sn = _numpy_quant(x)                   # each row is one group
+    assert s.shape == (96, 1)
+    assert (s[:, 0].view(np.uint32) == sn.view(np.uint32)).all()
+    assert (q == qn).all()
+    assert s[3, 0] == 0 and (q[3] == 0).all()
+    assert q[4, 17] == 127
+
+
+def test_per_token_dispatch_combine_identity(orc):
+    wl = W.get("decode_pt")
+    H = wl.hidden
+    x, _ = W.make_inputs(wl)
+    T = x.shape[0]
+    cfg = orc.Cfg(H, 4, 4, 1, 0, orc.SCORE_SIGMOID_NORM, [T, 0, 0, 0], group_size=H)
+    sd = -(-(H + 4) // 512) * 512
+    slots = np.arange(T, dtype=np.int32)[:, None]
+    dbuf = orc.dispatch(cfg, x, slots, T, sd)
+    q, s = orc.quantize_tokens(x, group_size=H)
+    assert (dbuf[:, :H].view(np.int8) == q).all()
+    assert (dbuf[:, H:H + 4].view(np.float32)[:, 0] == s[:, 0]).all()
+    y = orc.combine(cfg, dbuf, orc.FMT_Q8, slots, np.ones((T, 1), np.float32))
+    assert (y == f32_bits_to_bf16_torch(q.astype(np.float32) * s)).all()
