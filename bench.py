@@ -235,9 +235,62 @@ def run(args):
         },
         "wall_s_timed": wall,
     }
+    if args.workload == "global" and not args.no_decode:
+        res["decode_latency"] = decode_latency()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def decode_latency(n=200):
+    """Latency of one die's decode batch (96 tokens, hidden 7168, 256 experts,
+    top-8): the two-step path (route, dispatch, combine) against the
+    single-launch route+dispatch, and combine capped at 16 workgroups.  Each
+    call is bracketed by its own events; means over n calls."""
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+    wl = W.get("decode")
+    T, H, K = wl.tokens, wl.hidden, wl.K
+    plan = M.Plan.from_workload(wl)
+    b = plan.alloc("cuda:0")
+    x, logits = W.make_inputs(wl)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    lg = torch.from_numpy(logits).cuda()
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    rargs = (b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"], b["dropped"])
+    plan.route(lg, *rargs, b["workspace"])
+    plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+    plan.expert_stub(b["counts"], b["dispatch_buf"], b["combine_buf"], b["workspace"])
+    calls = {
+        "route": lambda: plan.route(lg, *rargs, b["workspace"]),
+        "dispatch": lambda: plan.dispatch(xd, b["slots"], b["dispatch_buf"]),
+        "route_dispatch_fused": lambda: plan.route_dispatch(lg, xd, *rargs, b["dispatch_buf"],
+                                                            b["workspace"]),
+        "combine": lambda: plan.combine(b["combine_buf"], M.FMT_BF16, b["slots"], b["topk_w"], y),
+        "combine_16wg": lambda: plan.combine_limited(b["combine_buf"], M.FMT_BF16, b["slots"],
+                                                     b["topk_w"], y, 16),
+    }
+    calls["launch_floor"] = lambda: y[:1, :8].zero_()  # one tiny torch kernel
+    res = {}
+    for name, f in calls.items():
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            f()
+            e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = statistics.fmean(1e3 * e0.elapsed_time(e1) for e0, e1 in ev)
+    res["two_step_us"] = res["route_us"] + res["dispatch_us"] + res["combine_us"]
+    res["fused_us"] = res["route_dispatch_fused_us"] + res["combine_us"]
+    res["workload"] = f"decode: {wl.description}"
+    return res
 
 
 def calib_copy(args):
@@ -335,6 +388,8 @@ def main():
     ap.add_argument("--workload", default="global")
     ap.add_argument("--combine-fmt", choices=["bf16", "q8"], default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=4 << 30)
@@ -356,6 +411,9 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy(args)
+        return
+    if args.decode_only:
+        print(json.dumps(decode_latency()), flush=True)
         return
     run(args)
 

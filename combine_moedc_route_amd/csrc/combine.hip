@@ -7,7 +7,8 @@
 // acc = +0; acc = fma(w_j, y_j, acc) over the token's entries in route
 // order, dropped entries skipped; BF16 round-to-nearest-even at the end.
 //
-// Mapping: one wave64 per token.  The token's H values are covered in
+// Mapping: one wave64 per token (a grid-stride loop when the caller caps
+// the number of workgroups).  The token's H values are covered in
 // groups of kChunks 512-value chunks (lane l holds values 512c + 8l .. +8
 // of chunk c).  Within a group the wave walks the K expert rows in route
 // order and, for each row, issues the loads of all kChunks chunks back to
@@ -45,10 +46,7 @@ __device__ __forceinline__ void store_nt16(uint16_t *p, const float (&acc)[8]) {
 }
 
 template <int K, bool Q8>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  const int lane = lane_id();
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
-  if (t >= a.T) return;
+__device__ __forceinline__ void combine_token(const CombineArgs &a, int64_t t, int lane) {
   const int H = a.H;
   int slot[K];
   float w[K];
@@ -95,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
           sc[c] = 0.0f;
           if (slot[k] >= 0 && e < H) {
             v[c] = load_nt8(row + e);
-            sc[c] = *reinterpret_cast<const float *>(row + H + 4 * (e >> 7));
+            sc[c] = *reinterpret_cast<const float *>(row + H + (a.per_token ? 0 : 4 * (e >> 7)));
           }
         }
 #pragma unroll
@@ -117,11 +115,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+template <int K, bool Q8>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int lane = lane_id();
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6); t < a.T;
+       t += stride) {
+    combine_token<K, Q8>(a, t, lane);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((a.T + kWavesPerBlock - 1) / kWavesPerBlock);
+  const int64_t need = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const unsigned grid = (unsigned)(need < a.max_blocks ? need : a.max_blocks);
   const bool q8 = a.fmt == MOEDC_FMT_Q8;
   switch (a.K) {
 #define MOEDC_CASE(k)                                                  \

@@ -27,8 +27,8 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 moedc_status validate_config(const moedc_config *c) {
   using namespace moedc;
   if (!c || !c->capacity) return MOEDC_ERR_INVALID_ARG;
-  if (c->group_size != kGroup) return MOEDC_ERR_UNSUPPORTED;
   if (c->hidden <= 0 || c->hidden % kGroup) return MOEDC_ERR_INVALID_ARG;
+  if (c->group_size != kGroup && c->group_size != c->hidden) return MOEDC_ERR_UNSUPPORTED;
   if (c->hidden > kMaxHidden) return MOEDC_ERR_UNSUPPORTED;
   if (c->max_tokens < 0) return MOEDC_ERR_INVALID_ARG;
   if (c->max_tokens > (1 << 24)) return MOEDC_ERR_UNSUPPORTED;
@@ -118,7 +118,7 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
     p->cfg.capacity = p->cap.data();
     p->cfg.replica_table = c.replica_table ? p->rep_table.data() : nullptr;
     p->K = c.top_k + c.num_shared;
-    p->G = c.hidden / kGroup;
+    p->G = c.hidden / c.group_size;
     p->slot_stride = round_up((int64_t)c.hidden + 4 * (int64_t)p->G, kSlotAlign);
     p->combine_stride = 2 * (int64_t)c.hidden;
     p->nblk_max = c.max_tokens > 0 ? (c.max_tokens + kRouteTokens - 1) / kRouteTokens : 1;
@@ -172,9 +172,14 @@ moedc_status moedc_plan_bind_workspace(const moedc_plan *p, void *ws, hipStream_
   return MOEDC_OK;
 }
 
-moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, int32_t *topk_ids,
-                         float *topk_w, int32_t *counts, int32_t *offsets, int32_t *slots,
-                         int32_t *dropped, void *ws, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moedc_status check_route(const moedc_plan *p, int32_t T, const float *logits,
+                         const int32_t *topk_ids, const float *topk_w, const int32_t *counts,
+                         const int32_t *offsets, const int32_t *slots, const int32_t *dropped,
+                         const void *ws) {
   if (!p || !counts || !offsets || !dropped || !ws) return MOEDC_ERR_INVALID_ARG;
   if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
   if (T > 0 && (!logits || !topk_ids || !topk_w || !slots)) return MOEDC_ERR_INVALID_ARG;
@@ -183,6 +188,22 @@ moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, in
   if (T > 0 && (!aligned16(logits) || !aligned4(topk_ids) || !aligned4(topk_w) ||
                 !aligned4(slots)))
     return MOEDC_ERR_ALIGN;
+  return MOEDC_OK;
+}
+
+moedc_status check_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,
+                            const int32_t *slots, const void *dbuf) {
+  if (!p) return MOEDC_ERR_INVALID_ARG;
+  if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
+  if (T == 0) return MOEDC_OK;
+  if (!x || !slots || !dbuf) return MOEDC_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dbuf) || !aligned4(slots)) return MOEDC_ERR_ALIGN;
+  return MOEDC_OK;
+}
+
+moedc::RouteArgs route_args(const moedc_plan *p, int32_t T, const float *logits,
+                            int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets,
+                            int32_t *slots, int32_t *dropped, void *ws) {
   moedc::RouteArgs a{};
   a.logits = logits;
   a.topk_ids = topk_ids;
@@ -204,17 +225,11 @@ moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, in
   a.KR = p->cfg.top_k;
   a.shared = p->cfg.num_shared;
   a.score_fn = p->cfg.score_fn;
-  const hipError_t e = moedc::launch_route(a, stream);
-  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+  return a;
 }
 
-moedc_status moedc_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,
-                            const int32_t *slots, void *dbuf, hipStream_t stream) {
-  if (!p) return MOEDC_ERR_INVALID_ARG;
-  if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
-  if (T == 0) return MOEDC_OK;
-  if (!x || !slots || !dbuf) return MOEDC_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(dbuf) || !aligned4(slots)) return MOEDC_ERR_ALIGN;
+moedc::DispatchArgs dispatch_args(const moedc_plan *p, int32_t T, const uint16_t *x,
+                                  const int32_t *slots, void *dbuf) {
   moedc::DispatchArgs a{};
   a.x = x;
   a.slots = slots;
@@ -224,15 +239,16 @@ moedc_status moedc_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,
   a.H = p->cfg.hidden;
   a.G = p->G;
   a.K = p->K;
-  const hipError_t e = moedc::launch_dispatch(a, stream);
-  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+  a.per_token = p->G == 1;
+  return a;
 }
 
-moedc_status moedc_combine(const moedc_plan *p, int32_t T, const void *eout, int32_t fmt,
-                           const int32_t *slots, const float *topk_w, uint16_t *y,
-                           hipStream_t stream) {
+moedc_status combine_impl(const moedc_plan *p, int32_t T, const void *eout, int32_t fmt,
+                          const int32_t *slots, const float *topk_w, uint16_t *y,
+                          int32_t max_blocks, hipStream_t stream) {
   if (!p) return MOEDC_ERR_INVALID_ARG;
   if (fmt != MOEDC_FMT_BF16 && fmt != MOEDC_FMT_Q8) return MOEDC_ERR_INVALID_ARG;
+  if (max_blocks < 1) return MOEDC_ERR_INVALID_ARG;
   if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
   if (T == 0) return MOEDC_OK;
   if (!eout || !slots || !topk_w || !y) return MOEDC_ERR_INVALID_ARG;
@@ -248,8 +264,66 @@ moedc_status moedc_combine(const moedc_plan *p, int32_t T, const void *eout, int
   a.H = p->cfg.hidden;
   a.K = p->K;
   a.fmt = fmt;
+  a.per_token = p->G == 1;
+  a.max_blocks = max_blocks;
   const hipError_t e = moedc::launch_combine(a, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, int32_t *topk_ids,
+                         float *topk_w, int32_t *counts, int32_t *offsets, int32_t *slots,
+                         int32_t *dropped, void *ws, hipStream_t stream) {
+  const moedc_status st =
+      check_route(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
+  if (st != MOEDC_OK) return st;
+  const hipError_t e = moedc::launch_route(
+      route_args(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws), stream);
+  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+}
+
+moedc_status moedc_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,
+                            const int32_t *slots, void *dbuf, hipStream_t stream) {
+  const moedc_status st = check_dispatch(p, T, x, slots, dbuf);
+  if (st != MOEDC_OK || T == 0) return st;
+  const hipError_t e = moedc::launch_dispatch(dispatch_args(p, T, x, slots, dbuf), stream);
+  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+}
+
+moedc_status moedc_route_dispatch(const moedc_plan *p, int32_t T, const float *logits,
+                                  const uint16_t *x, int32_t *topk_ids, float *topk_w,
+                                  int32_t *counts, int32_t *offsets, int32_t *slots,
+                                  int32_t *dropped, void *dbuf, void *ws, hipStream_t stream) {
+  moedc_status st =
+      check_route(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
+  if (st == MOEDC_OK) st = check_dispatch(p, T, x, slots, dbuf);
+  if (st != MOEDC_OK) return st;
+  const moedc::RouteArgs ra =
+      route_args(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
+  const moedc::DispatchArgs da = dispatch_args(p, T, x, slots, dbuf);
+  hipError_t e;
+  if (T > 0 && T <= moedc::kFusedMaxTokens) {
+    e = moedc::launch_route_dispatch_fused(ra, da, stream);
+  } else {
+    e = moedc::launch_route(ra, stream);
+    if (e == hipSuccess && T > 0) e = moedc::launch_dispatch(da, stream);
+  }
+  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+}
+
+moedc_status moedc_combine(const moedc_plan *p, int32_t T, const void *eout, int32_t fmt,
+                           const int32_t *slots, const float *topk_w, uint16_t *y,
+                           hipStream_t stream) {
+  return combine_impl(p, T, eout, fmt, slots, topk_w, y, INT32_MAX, stream);
+}
+
+moedc_status moedc_combine_limited(const moedc_plan *p, int32_t T, const void *eout, int32_t fmt,
+                                   const int32_t *slots, const float *topk_w, uint16_t *y,
+                                   int32_t max_workgroups, hipStream_t stream) {
+  return combine_impl(p, T, eout, fmt, slots, topk_w, y, max_workgroups, stream);
 }
 
 moedc_status moedc_expert_stub(const moedc_plan *p, const int32_t *counts, const void *dbuf,
@@ -268,6 +342,7 @@ moedc_status moedc_expert_stub(const moedc_plan *p, const int32_t *counts, const
   a.total_slots = p->total_slots;
   a.H = p->cfg.hidden;
   a.P = p->cfg.num_phys_experts;
+  a.per_token = p->G == 1;
   const hipError_t e = moedc::launch_stub(a, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }

@@ -18,6 +18,7 @@ constexpr int kMaxExperts = 1024;    // logical and physical
 constexpr int kMaxK = 16;            // entries per token
 constexpr int kMaxReplicas = 8;
 constexpr int kRouteTokens = 64;     // tokens per route block (4 lanes per token)
+constexpr int kFusedMaxTokens = 256; // largest batch of the single-launch route + dispatch
 constexpr int64_t kSlotAlign = 512;  // dispatch slot stride granularity
 constexpr int64_t kWsAlign = 256;
 
@@ -53,6 +54,7 @@ struct DispatchArgs {
   uint8_t *dbuf;
   int64_t slot_stride;
   int32_t T, H, G, K;
+  int32_t per_token;  // one scale per token (G == 1) instead of per 128 values
 };
 
 struct CombineArgs {
@@ -62,6 +64,8 @@ struct CombineArgs {
   uint16_t *y;
   int64_t eout_stride;  // bytes per slot row
   int32_t T, H, K, fmt;
+  int32_t per_token;    // Q8 input: one scale per token
+  int32_t max_blocks;   // grid cap (workgroups of 4 token waves); >= 1
 };
 
 struct StubArgs {
@@ -74,12 +78,15 @@ struct StubArgs {
   int64_t ebuf_stride;
   int64_t total_slots;
   int32_t H, P;
+  int32_t per_token;
 };
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_stub(const StubArgs &a, hipStream_t s);
+hipError_t launch_route_dispatch_fused(const RouteArgs &ra, const DispatchArgs &da,
+                                       hipStream_t s);
 
 }  // namespace moedc
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void stub_kernel(StubArgs a) {
     const int e = c * 512 + lane * 8;
     if (e >= H) continue;
     const uint2 q = *reinterpret_cast<const uint2 *>(src + e);
-    const float sc = *reinterpret_cast<const float *>(src + H + 4 * (e >> 7));
+    const float sc = *reinterpret_cast<const float *>(src + H + (a.per_token ? 0 : 4 * (e >> 7)));
     float o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

@@ -24,8 +24,8 @@ FMT_BF16, FMT_Q8 = 0, 1
 EXPORTS = (
     "moedc_plan_create", "moedc_plan_destroy", "moedc_plan_sizes",
     "moedc_plan_bind_workspace", "moedc_route", "moedc_dispatch",
-    "moedc_combine", "moedc_expert_stub", "moedc_status_string",
-    "moedc_last_hip_error",
+    "moedc_combine", "moedc_route_dispatch", "moedc_combine_limited",
+    "moedc_expert_stub", "moedc_status_string", "moedc_last_hip_error",
 )
 
 
@@ -104,6 +104,10 @@ def load_library(path):
     L.moedc_dispatch.restype = i32
     L.moedc_combine.argtypes = [P, i32, P, i32, P, P, P, P]
     L.moedc_combine.restype = i32
+    L.moedc_route_dispatch.argtypes = [P, i32, P, P, P, P, P, P, P, P, P, P, P]
+    L.moedc_route_dispatch.restype = i32
+    L.moedc_combine_limited.argtypes = [P, i32, P, i32, P, P, P, i32, P]
+    L.moedc_combine_limited.restype = i32
     L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
     L.moedc_expert_stub.restype = i32
     L.moedc_status_string.argtypes = [i32]
@@ -171,7 +175,8 @@ class Plan:
                    hidden=wl.hidden, num_logical=wl.num_logical,
                    num_phys=wl.num_phys, top_k=wl.top_k, num_shared=wl.num_shared,
                    score_fn=wl.score_fn, capacity=wl.capacity,
-                   replica_table=wl.replica_table)
+                   replica_table=wl.replica_table,
+                   group_size=getattr(wl, "group_size", 128))
 
     def close(self):
         if self._h is not None:
@@ -229,6 +234,21 @@ class Plan:
         T = y.shape[0] if num_tokens is None else num_tokens
         _check(lib().moedc_combine(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
                                    _ptr(topk_w), _ptr(y), _stream(stream)), "moedc_combine")
+
+    def route_dispatch(self, logits, x, topk_ids, topk_w, counts, offsets, slots, dropped,
+                       dispatch_buf, workspace, num_tokens: Optional[int] = None, stream=None):
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moedc_route_dispatch(
+            self._h, T, _ptr(logits), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
+            _ptr(offsets), _ptr(slots), _ptr(dropped), _ptr(dispatch_buf), _ptr(workspace),
+            _stream(stream)), "moedc_route_dispatch")
+
+    def combine_limited(self, expert_out, fmt: int, slots, topk_w, y, max_workgroups: int,
+                        num_tokens: Optional[int] = None, stream=None):
+        T = y.shape[0] if num_tokens is None else num_tokens
+        _check(lib().moedc_combine_limited(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
+                                           _ptr(topk_w), _ptr(y), max_workgroups,
+                                           _stream(stream)), "moedc_combine_limited")
 
     def expert_stub(self, counts, dispatch_buf, combine_buf, workspace, stream=None):
         _check(lib().moedc_expert_stub(self._h, _ptr(counts), _ptr(dispatch_buf),

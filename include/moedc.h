@@ -68,7 +68,7 @@ typedef enum moedc_elem_fmt {
 typedef struct moedc_config {
   int32_t max_tokens;          /* largest token count any call will pass (>= 0) */
   int32_t hidden;              /* H: multiple of 128, 128..8192 */
-  int32_t group_size;          /* quantization group; must be 128 */
+  int32_t group_size;          /* values per fp32 scale: 128, or hidden (one scale per token) */
   int32_t num_logical_experts; /* E_log: logits per token, 1..1024 */
   int32_t num_phys_experts;    /* E_phys: physical experts incl. replicas and shared, 1..1024 */
   int32_t top_k;               /* routed picks per token, 1..E_log */
@@ -90,11 +90,11 @@ typedef struct moedc_sizes {
   int64_t workspace_bytes;      /* device workspace for route/stub (bind once) */
   int64_t dispatch_buf_bytes;   /* total_slots * slot_stride */
   int64_t combine_buf_bytes;    /* total_slots * combine_slot_stride */
-  int64_t slot_stride;          /* dispatch slot: round_up(H + 4*H/128, 512) bytes */
+  int64_t slot_stride;          /* dispatch slot: round_up(H + 4*G, 512) bytes */
   int64_t combine_slot_stride;  /* BF16 combine slot: 2*H bytes */
   int64_t total_slots;          /* sum of capacities */
   int32_t k;                    /* entries per token: top_k + num_shared */
-  int32_t num_groups;           /* H / 128 */
+  int32_t num_groups;           /* G = H / group_size */
 } moedc_sizes;
 
 typedef struct moedc_plan moedc_plan;
@@ -148,11 +148,13 @@ moedc_status moedc_route(const moedc_plan *plan, int32_t num_tokens,
  * store of each token into each of its slots ("FusedDispatch and
  * FusedCombine": quantize before sending, write into pre-allocated
  * receiver buffers, token-granular load / quantize / write pipeline).
- * Per token and 128-value group: amax = max |x|; scale = amax / 127 in IEEE
- * fp32; q = clamp(round-half-even(x / scale), -127, 127) with a correctly
- * rounded fp32 quotient (scale 0 gives q 0).  Slot s occupies bytes
+ * Per token and group (128 values, or the whole token when group_size ==
+ * hidden, following "INT8 Quantization": per-token dynamic activation
+ * scales): amax = max |x|; scale = amax / 127 in IEEE fp32; q =
+ * clamp(round-half-even(x / scale), -127, 127) with a correctly rounded
+ * fp32 quotient (scale 0 gives q 0).  Slot s occupies bytes
  * [s*slot_stride, (s+1)*slot_stride) of dispatch_buf: INT8 payload at
- * [0, H), fp32 scales (little-endian) at [H, H + 4*H/128); the rest of the
+ * [0, H), G fp32 scales (little-endian) at [H, H + 4*G); the rest of the
  * slot and slots no token maps to are not written.  Entries with slot -1
  * are skipped.
  * x: BF16 [num_tokens][H] (16-byte aligned); slots: from moedc_route;
@@ -177,6 +179,38 @@ moedc_status moedc_combine(const moedc_plan *plan, int32_t num_tokens,
                            const void *expert_out, int32_t fmt,
                            const int32_t *slots, const float *topk_w,
                            uint16_t *y, hipStream_t stream);
+
+/*
+ * Routing and dispatch in one call, for small decode batches.  Same outputs
+ * and the same dispatch buffer bytes as moedc_route followed by
+ * moedc_dispatch (softmax gates may differ in the last bits: the softmax
+ * denominator is summed in a different order; sigmoid-normalised gates are
+ * identical).  For 1 <= num_tokens <= 256 it is a single kernel launch in
+ * which every workgroup recomputes the routing of the whole batch and then
+ * quantizes and stores one token ("Decode Phase": 96 tokens per die;
+ * "FusedDispatch and FusedCombine": routing metadata fused with the token
+ * exchange); larger batches run the two-step path.  Arguments, layouts,
+ * alignment and errors are those of moedc_route and moedc_dispatch.
+ */
+moedc_status moedc_route_dispatch(const moedc_plan *plan, int32_t num_tokens,
+                                  const float *logits, const uint16_t *x,
+                                  int32_t *topk_ids, float *topk_w, int32_t *counts,
+                                  int32_t *offsets, int32_t *slots, int32_t *dropped,
+                                  void *dispatch_buf, void *workspace, hipStream_t stream);
+
+/*
+ * moedc_combine on at most max_workgroups workgroups (each runs 4 token
+ * waves and loops over the batch), leaving the other compute units to
+ * concurrent work on other streams -- the pages' decode pipeline gives the
+ * MoE path a fixed share of the cores ("Micro-batch Decode Pipeline" of the
+ * CloudMatrix384 article).  Output identical to moedc_combine.
+ * Errors: as moedc_combine; INVALID_ARG if max_workgroups < 1.
+ */
+moedc_status moedc_combine_limited(const moedc_plan *plan, int32_t num_tokens,
+                                   const void *expert_out, int32_t fmt,
+                                   const int32_t *slots, const float *topk_w,
+                                   uint16_t *y, int32_t max_workgroups,
+                                   hipStream_t stream);
 
 /*
  * Stand-in expert (not a step of the method; it fills combine inputs so the

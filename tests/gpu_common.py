@@ -88,10 +88,10 @@ def gpu_dispatch(plan, x_bits, slots, sentinel=SENTINEL):
     return dbuf
 
 
-def check_dispatch_tokens(dbuf, x_bits, slots, tokens, H):
+def check_dispatch_tokens(dbuf, x_bits, slots, tokens, H, group_size=128):
     """Bit-exact payload + scales of every kept slot of the given tokens."""
-    G = H // 128
-    q, s = oracle.quantize_tokens(x_bits[tokens])
+    G = H // group_size
+    q, s = oracle.quantize_tokens(x_bits[tokens], group_size)
     want = np.concatenate([q.view(np.uint8), s.view(np.uint8)], axis=1)   # [n][H+4G]
     rows, owner = [], []
     for i, t in enumerate(tokens):
@@ -108,9 +108,9 @@ def check_dispatch_tokens(dbuf, x_bits, slots, tokens, H):
     return len(rows)
 
 
-def check_dispatch_untouched(dbuf, slots, H, sentinel=SENTINEL):
+def check_dispatch_untouched(dbuf, slots, H, sentinel=SENTINEL, group_size=128):
     """Unoccupied slots and slot tails keep the sentinel."""
-    G = H // 128
+    G = H // group_size
     S = dbuf.shape[0]
     occ = torch.zeros(S, dtype=torch.bool, device="cuda")
     sl = torch.from_numpy(slots[slots >= 0].astype(np.int64)).cuda()

@@ -49,6 +49,7 @@ def plan_status(**kw):
 def test_plan_validation():
     assert plan_status() == M.OK
     assert plan_status(group_size=64) == M.ERR_UNSUPPORTED
+    assert plan_status(group_size=256) == M.OK                      # one scale per token
     assert plan_status(hidden=200) == M.ERR_INVALID_ARG
     assert plan_status(hidden=8192 + 128) == M.ERR_UNSUPPORTED
     assert plan_status(top_k=0) == M.ERR_INVALID_ARG
@@ -90,6 +91,8 @@ def test_plan_sizes_match_page_slot_format():
     assert s.workspace_bytes >= 4 * 256 * (30720 // 256)
     # The pages' per-die budget: 30720-slot windows of both buffers = 645 MiB.
     assert 30720 * (s.slot_stride + s.combine_slot_stride) == 645 * 2 ** 20
+    s = M.Plan.from_workload(W.get("decode_pt")).sizes
+    assert s.num_groups == 1 and s.slot_stride == 7680               # 7172 B -> 7.5 KiB
     for name in ("tiny", "ragged", "prefill", "skewed", "replica_shared"):
         wl = W.get(name)
         s = M.Plan.from_workload(wl).sizes
@@ -124,6 +127,12 @@ def test_call_validation_returns_before_launch():
     assert L.moedc_combine(h, 3, a16, M.FMT_Q8, a16, a16, a1, None) == M.ERR_ALIGN
     assert L.moedc_combine(h, 99, a16, M.FMT_Q8, a16, a16, a16, None) == M.ERR_SHAPE
     assert L.moedc_expert_stub(h, a16, a16, a16, None, None) == M.ERR_INVALID_ARG
+    assert L.moedc_combine_limited(h, 3, a16, M.FMT_BF16, a16, a16, a16, 0, None) == \
+        M.ERR_INVALID_ARG
+    assert L.moedc_route_dispatch(h, 65, a16, a16, a16, a16, a16, a16, a16, a16, a16, a16,
+                                  None) == M.ERR_SHAPE
+    assert L.moedc_route_dispatch(h, 3, a16, a1, a16, a16, a16, a16, a16, a16, a16, a16,
+                                  None) == M.ERR_ALIGN
     assert L.moedc_plan_bind_workspace(h, a1, None) == M.ERR_ALIGN
     assert L.moedc_plan_sizes(None, None) == M.ERR_INVALID_ARG
     out = C.c_void_p(123)

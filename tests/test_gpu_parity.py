@@ -17,7 +17,7 @@ from gpu_common import (SENTINEL, U, bf16_to_f32, check_dispatch_tokens,
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["tiny", "decode", "mid", "ragged", "overflow", "replica_shared"]
+SMALL = ["tiny", "decode", "decode_pt", "mid", "ragged", "overflow", "replica_shared"]
 FULL = ["global", "skewed", "prefill"]
 
 
@@ -100,8 +100,9 @@ def test_dispatch_parity(name):
     wl, x, logits, plan, cfg = setup(name)
     r = oracle.route(cfg, logits)
     dbuf = gpu_dispatch(plan, x, r["slots"])
-    n = check_dispatch_tokens(dbuf, x, r["slots"], np.arange(x.shape[0]), wl.hidden)
-    check_dispatch_untouched(dbuf, r["slots"], wl.hidden)
+    n = check_dispatch_tokens(dbuf, x, r["slots"], np.arange(x.shape[0]), wl.hidden,
+                              wl.group_size)
+    check_dispatch_untouched(dbuf, r["slots"], wl.hidden, group_size=wl.group_size)
     # Whole-buffer byte equality against the oracle's own dispatch.
     s = plan.sizes
     ref = np.full((s.total_slots, s.slot_stride), SENTINEL, np.uint8)
@@ -217,7 +218,7 @@ def test_combine_parity_full_size(name):
 
 # ------------------------------------------------------------------ expert stand-in
 
-@pytest.mark.parametrize("name", ["decode", "ragged", "replica_shared", "overflow"])
+@pytest.mark.parametrize("name", ["decode", "decode_pt", "ragged", "replica_shared", "overflow"])
 def test_expert_stub_parity(name):
     wl, x, logits, plan, cfg = setup(name)
     r = oracle.route(cfg, logits)
@@ -256,7 +257,7 @@ def _e2e(name):
     s = plan.sizes
     toks = sample_tokens(T, 256, 8)
     check_dispatch_tokens(b["dispatch_buf"].view(s.total_slots, s.slot_stride), x, r["slots"],
-                          toks, H)
+                          toks, H, wl.group_size)
     # Final output: GPU gates differ from the oracle's by the gate tolerance,
     # so the bound is 1 BF16 ulp + sum_k |dw_k||y_k| + 2K u sum_k |w_k y_k|.
     dref = oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride)
@@ -272,8 +273,9 @@ def _e2e(name):
             if sl < 0:
                 continue
             if identity:
+                gs = wl.group_size
                 q = dref[sl, :H].view(np.int8).astype(np.float32)
-                sc = np.repeat(dref[sl, H:H + 4 * (H // 128)].view(np.float32), 128)
+                sc = np.repeat(dref[sl, H:H + 4 * (H // gs)].view(np.float32), gs)
                 yk[k] = (q * sc).astype(np.float64)
             else:
                 yk[k] = bf16_to_f32(eref[sl]).astype(np.float64)
@@ -289,3 +291,67 @@ def _e2e(name):
 @pytest.mark.parametrize("name", SMALL + ["global"])
 def test_end_to_end(name):
     _e2e(name)
+
+
+# ------------------------------------------------------------------ fused route + dispatch
+
+def _fused_case(wl, logits, x):
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    T, K, P = x.shape[0], wl.K, wl.num_phys
+    s = plan.sizes
+    ws = torch.empty(s.workspace_bytes, dtype=torch.uint8, device="cuda")
+    plan.bind_workspace(ws)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    out = dict(topk_ids=torch.full((T, K), -7, **i32),
+               topk_w=torch.full((T, K), -7.0, dtype=torch.float32, device="cuda"),
+               counts=torch.full((P,), -7, **i32), offsets=torch.full((P + 1,), -7, **i32),
+               slots=torch.full((T, K), -7, **i32), dropped=torch.full((1,), -7, **i32))
+    dbuf = torch.full((s.total_slots, s.slot_stride), SENTINEL, dtype=torch.uint8, device="cuda")
+    plan.route_dispatch(dev(logits), dev_i16(x), out["topk_ids"], out["topk_w"], out["counts"],
+                        out["offsets"], out["slots"], out["dropped"], dbuf, ws)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    got["dropped"] = int(got["dropped"][0])
+    want = oracle.route(cfg, logits)
+    compare_route(wl, got, want)
+    ref = np.full((s.total_slots, s.slot_stride), SENTINEL, np.uint8)
+    oracle.dispatch(cfg, x, want["slots"], s.total_slots, s.slot_stride, buf=ref)
+    assert np.array_equal(dbuf.cpu().numpy(), ref)
+    return got
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode_pt", "mid", "replica_shared"])
+def test_route_dispatch_fused_parity(name):
+    wl, x, logits, plan, cfg = setup(name)
+    _fused_case(wl, logits, x)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 200, 256])
+@pytest.mark.parametrize("variant", ["softmax40", "sigmoid_shared_rep", "drops_pertoken"])
+def test_route_dispatch_fused_sizes(T, variant):
+    base = W.get({"softmax40": "ragged", "sigmoid_shared_rep": "replica_shared",
+                  "drops_pertoken": "overflow"}[variant])
+    wl = W.with_tokens(base, T)
+    if variant == "drops_pertoken":
+        wl = W.Workload("d", "", T, 512, 16, 16, 4, 0, W.SCORE_SIGMOID_NORM,
+                        np.full(16, max(1, T // 8), np.int32), None, 13, "zipf",
+                        ("fraction", 0.05, 1000.0), group_size=512)
+    log(f"[case] fused {variant} T={T}")
+    x, logits = W.make_inputs(wl, T)
+    got = _fused_case(wl, logits, x)
+    if variant == "drops_pertoken" and T >= 64:
+        assert got["dropped"] > 0
+
+
+@pytest.mark.parametrize("workgroups", [1, 3, 16, 10 ** 6])
+@pytest.mark.parametrize("fmt", [M.FMT_BF16, M.FMT_Q8])
+def test_combine_limited_matches_combine(workgroups, fmt):
+    wl, x, logits, plan, cfg = setup("decode_pt" if fmt == M.FMT_Q8 else "decode")
+    r = oracle.route(cfg, logits)
+    dref, ebuf = _combine_inputs(wl, x, cfg, plan, r)
+    src = dev_i16(ebuf) if fmt == M.FMT_BF16 else dev(dref)
+    want = oracle.combine(cfg, ebuf if fmt == M.FMT_BF16 else dref, fmt, r["slots"], r["topk_w"])
+    y = torch.full((x.shape[0], wl.hidden), -1, dtype=torch.int16, device="cuda")
+    plan.combine_limited(src, fmt, dev(r["slots"]), dev(r["topk_w"]), y, workgroups)
+    assert np.array_equal(host_u16(y), want)
