@@ -193,6 +193,16 @@ def make_expert_out_bf16(seed: int, rows: int, hidden: int) -> np.ndarray:
     return _to_bf16_bits(rng.standard_normal((rows, hidden), dtype=np.float32))
 
 
+def make_expert_weights(seed: int, num_phys: int, hidden: int):
+    """Synthetic W8A8 expert weights: int8 [P][H][H] uniform in [-127, 127]
+    and per-output-channel fp32 scales ~ U[0.5, 1.5) / (127 * sqrt(H))."""
+    rng = np.random.default_rng(seed)
+    W = rng.integers(-127, 128, size=(num_phys, hidden, hidden), dtype=np.int8)
+    ws = (rng.random((num_phys, hidden), dtype=np.float32) + np.float32(0.5)) / \
+        np.float32(127.0 * np.sqrt(hidden))
+    return W, ws.astype(np.float32)
+
+
 def make_gates(seed: int, T: int, K: int) -> np.ndarray:
     """Random positive fp32 gate weights for combine-only cases."""
     rng = np.random.default_rng(seed)

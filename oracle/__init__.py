@@ -59,6 +59,7 @@ def lib():
         L.orc_dispatch.argtypes = [C.POINTER(OrcCfg), i32, P, P, P, i64]
         L.orc_expert_stub.argtypes = [C.POINTER(OrcCfg), P, P, i64, P, i64]
         L.orc_combine.argtypes = [C.POINTER(OrcCfg), i32, P, i32, i64, P, P, P]
+        L.orc_expert_w8a8.argtypes = [C.POINTER(OrcCfg), P, P, i64, P, P, P, i64]
         _lib = L
     return _lib
 
@@ -173,6 +174,20 @@ def expert_stub(cfg: Cfg, counts, dbuf, slot_stride):
     ebuf = np.zeros((S, H), np.uint16)
     _check(lib().orc_expert_stub(C.byref(cfg.c), _p(counts), _p(dbuf),
                                  slot_stride, _p(ebuf), 2 * H), "expert_stub")
+    return ebuf
+
+
+def expert_w8a8(cfg: Cfg, counts, dbuf, slot_stride, W, w_scale, ebuf=None):
+    """One W8A8 linear layer per physical expert over the occupied slots.
+    W: int8 [P][H][H]; w_scale: fp32 [P][H]; returns ebuf uint16 [S][H]."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    W = np.ascontiguousarray(W, dtype=np.int8)
+    w_scale = np.ascontiguousarray(w_scale, dtype=np.float32)
+    H = cfg.hidden
+    if ebuf is None:
+        ebuf = np.zeros((dbuf.shape[0], H), np.uint16)
+    _check(lib().orc_expert_w8a8(C.byref(cfg.c), _p(counts), _p(dbuf), slot_stride,
+                                 _p(W), _p(w_scale), _p(ebuf), 2 * H), "expert_w8a8")
     return ebuf
 
 

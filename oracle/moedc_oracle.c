@@ -313,6 +313,40 @@ int orc_expert_stub(const orc_cfg *c, const int32_t *counts,
   return ORC_OK;
 }
 
+/* ---- expert: one W8A8 linear layer -------------------------------------- */
+
+int orc_expert_w8a8(const orc_cfg *c, const int32_t *counts, const uint8_t *dbuf,
+                    int64_t slot_stride, const int8_t *W, const float *w_scale,
+                    uint16_t *ebuf, int64_t ebuf_stride) {
+  int rc = orc_check_cfg(c);
+  if (rc) return rc;
+  const int32_t H = c->hidden, gs = c->group_size, G = H / gs;
+  int64_t base = 0;
+  for (int32_t p = 0; p < c->num_phys; ++p) {
+    int32_t used = counts[p] < c->capacity[p] ? counts[p] : c->capacity[p];
+    const int8_t *Wp = W + (int64_t)p * H * H;
+    for (int32_t j = 0; j < used; ++j) {
+      const uint8_t *row = dbuf + (base + j) * slot_stride;
+      const int8_t *q = (const int8_t *)row;
+      uint16_t *out = (uint16_t *)((uint8_t *)ebuf + (base + j) * ebuf_stride);
+      for (int32_t n = 0; n < H; ++n) {
+        const int8_t *w = Wp + (int64_t)n * H;
+        float acc = 0.0f;
+        for (int32_t g = 0; g < G; ++g) {
+          int32_t isum = 0;  /* |isum| <= H * 127 * 127 < 2^31 for H <= 8192 */
+          for (int32_t k = g * gs; k < (g + 1) * gs; ++k) isum += (int32_t)q[k] * (int32_t)w[k];
+          float sx;
+          memcpy(&sx, row + H + 4 * g, sizeof sx);
+          acc = fmaf(sx, (float)isum, acc);
+        }
+        out[n] = orc_f32_to_bf16(acc * w_scale[(int64_t)p * H + n]);
+      }
+    }
+    base += c->capacity[p];
+  }
+  return ORC_OK;
+}
+
 /* ---- combine ----------------------------------------------------------- */
 
 int orc_combine(const orc_cfg *c, int32_t T, const void *eout, int32_t fmt,

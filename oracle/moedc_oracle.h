@@ -88,6 +88,19 @@ int orc_expert_stub(const orc_cfg *c, const int32_t *counts,
                     const uint8_t *dbuf, int64_t slot_stride,
                     uint16_t *ebuf, int64_t ebuf_stride);
 
+/* Stand-in expert with real arithmetic, one W8A8 linear layer per physical
+ * expert (hidden -> hidden): for each occupied slot row of expert p and
+ * output channel n, with q the row's INT8 payload and s_x its scales,
+ *   isum_g = sum over group g of q[k] * W[p][n][k]   (exact int32)
+ *   acc = +0; acc = fmaf(s_x[g], (float)isum_g, acc) for g ascending
+ *   y[n] = bf16(acc * w_scale[p][n])
+ * W is int8 [num_phys][H][H] (row n = output channel), w_scale fp32
+ * [num_phys][H].  Weights per output channel, activations per token or per
+ * group ("INT8 Quantization": mixed granularity). */
+int orc_expert_w8a8(const orc_cfg *c, const int32_t *counts, const uint8_t *dbuf,
+                    int64_t slot_stride, const int8_t *W, const float *w_scale,
+                    uint16_t *ebuf, int64_t ebuf_stride);
+
 /* Combine: per token, fp32 multiply-add chain over its slots in route
  * order (dropped slots skipped), rounded once to BF16. */
 int orc_combine(const orc_cfg *c, int32_t T, const void *eout, int32_t fmt,

@@ -459,3 +459,95 @@ def test_per_token_dispatch_combine_identity(orc):
     assert (dbuf[:, H:H + 4].view(np.float32)[:, 0] == s[:, 0]).all()
     y = orc.combine(cfg, dbuf, orc.FMT_Q8, slots, np.ones((T, 1), np.float32))
     assert (y == f32_bits_to_bf16_torch(q.astype(np.float32) * s)).all()
+
+
+# ---------------------------------------------------------------- expert W8A8 linear
+
+def _expert_setup(orc, H, gs, T=20, P=3, seed=0):
+    wl = W.Workload("e", "", T, H, P, P, 1, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(P, T, np.int32), None, seed, "normal", group_size=gs)
+    cfg = orc.Cfg.from_workload(wl)
+    x, _ = W.make_inputs(wl)
+    sd = -(-(H + 4 * (H // gs)) // 512) * 512
+    counts = np.array([T, T // 2, 0][:P], np.int32)
+    slots = np.full((T, 1), -1, np.int32)
+    slots[:, 0] = np.arange(T)                          # expert 0 window
+    dbuf = orc.dispatch(cfg, x, slots, P * T, sd)
+    if P > 1:
+        dbuf[T:T + T // 2] = dbuf[:T // 2]              # expert 1 holds copies
+    return cfg, x, dbuf, sd, counts
+
+
+@pytest.mark.parametrize("H,gs", [(256, 128), (384, 384), (512, 128)])
+def test_expert_w8a8_exact_bound(orc, H, gs):
+    cfg, x, dbuf, sd, counts = _expert_setup(orc, H, gs)
+    Wt, ws = W.make_expert_weights(3, 3, H)
+    y = orc.expert_w8a8(cfg, counts, dbuf, sd, Wt, ws)
+    G = H // gs
+    T = x.shape[0]
+    for p, base, n_rows in ((0, 0, counts[0]), (1, T, counts[1])):
+        q = dbuf[base:base + n_rows, :H].view(np.int8).astype(np.int64)
+        sx = dbuf[base:base + n_rows, H:H + 4 * G].view(np.float32).astype(np.float64)
+        isum = np.stack([q[:, g * gs:(g + 1) * gs] @ Wt[p][:, g * gs:(g + 1) * gs].T.astype(np.int64)
+                         for g in range(G)], axis=2)    # [rows][n][g], exact
+        exact = (isum * sx[:, None, :]).sum(2) * ws[p].astype(np.float64)[None, :]
+        mag = (np.abs(isum) * np.abs(sx[:, None, :])).sum(2) * ws[p][None, :]
+        got = bf16_to_f32(y[base:base + n_rows]).astype(np.float64)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(got), 1e-30))) - 7)
+        assert (np.abs(got - exact) <= 0.5 * ulp + (G + 2) * U * mag + 1e-38).all()
+    assert (y[2 * T:] == 0).all()                       # expert 2 has no tokens
+
+
+def test_expert_w8a8_identity_weights_give_dequant(orc):
+    H, gs = 256, 128
+    cfg, x, dbuf, sd, counts = _expert_setup(orc, H, gs)
+    Wt = np.zeros((3, H, H), np.int8)
+    Wt[:, np.arange(H), np.arange(H)] = 1
+    y = orc.expert_w8a8(cfg, counts, dbuf, sd, Wt, np.ones((3, H), np.float32))
+    n = counts[0]
+    q = dbuf[:n, :H].view(np.int8).astype(np.float32)
+    s = np.repeat(dbuf[:n, H:H + 8].view(np.float32), gs, axis=1)
+    assert (y[:n] == f32_bits_to_bf16_torch(q * s)).all()
+
+
+def test_expert_w8a8_single_weight_picks_one_input(orc):
+    H, gs = 256, 128
+    cfg, x, dbuf, sd, counts = _expert_setup(orc, H, gs)
+    Wt = np.zeros((3, H, H), np.int8)
+    Wt[0, 7, 200] = 1                                   # out channel 7 <- input 200
+    ws = np.full((3, H), 2.0, np.float32)
+    y = orc.expert_w8a8(cfg, counts, dbuf, sd, Wt, ws)
+    n = counts[0]
+    q = dbuf[:n, 200].view(np.int8).astype(np.float32)
+    s = dbuf[:n, H + 4:H + 8].view(np.float32)[:, 0]    # group 1 holds input 200
+    assert (y[:n, 7] == f32_bits_to_bf16_torch((s * q) * np.float32(2.0))).all()
+    assert (np.delete(y[:n], 7, axis=1) == 0).all()
+
+
+def test_expert_w8a8_per_token_large_sum_rounds_like_float32(orc):
+    H = 2048                                             # isum up to 33e6 > 2^24
+    cfg, x, dbuf, sd, counts = _expert_setup(orc, H, H, T=4, P=1)
+    dbuf[:, :H] = np.uint8(127)
+    dbuf[1, 5] = np.uint8(126)                           # make the sums odd-ish
+    dbuf[:, H:H + 4] = np.frombuffer(np.float32(0.75).tobytes(), np.uint8)
+    Wt = np.full((1, H, H), 127, np.int8)
+    Wt[0, 3, :9] = 125
+    ws = np.full((1, H), 1.0 / 3, np.float32)
+    y = orc.expert_w8a8(cfg, np.array([4], np.int32), dbuf, sd, Wt, ws)
+    isum = dbuf[:4, :H].view(np.int8).astype(np.int64) @ Wt[0].T.astype(np.int64)
+    want = f32_bits_to_bf16_torch((np.float32(0.75) * isum.astype(np.float32)) * ws[0][None, :])
+    assert (y == want).all()
+
+
+def test_expert_w8a8_per_token_random_large_sums(orc):
+    H = 4096                                             # |isum| well beyond 2^24
+    cfg, x, dbuf, sd, counts = _expert_setup(orc, H, H, T=6, P=1, seed=5)
+    rng = np.random.default_rng(9)
+    dbuf[:, :H] = rng.integers(100, 128, (6, H)).astype(np.int8).view(np.uint8)
+    Wt = rng.integers(100, 128, (1, H, H)).astype(np.int8)
+    ws = np.full((1, H), 0.001, np.float32)
+    y = orc.expert_w8a8(cfg, np.array([6], np.int32), dbuf, sd, Wt, ws)
+    isum = dbuf[:6, :H].view(np.int8).astype(np.int64) @ Wt[0].T.astype(np.int64)
+    sx = dbuf[:6, H:H + 4].view(np.float32)
+    want = f32_bits_to_bf16_torch((sx * isum.astype(np.float32)) * ws[0][None, :])
+    assert (y == want).all()
