@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 METRIC = ("dispatch+combine µs and tokens/s at 30720×7168 top-8/256; "
           "% of HBM peak GB/s")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -235,6 +236,8 @@ def run(args):
         },
         "wall_s_timed": wall,
     }
+    if args.workload == "global" and not args.no_expert:
+        res["expert_gemm"] = expert_gemm(plan, wl, counts, sets[0][0], sets[0][1], ws)
     if args.workload == "global" and not args.no_decode:
         res["decode_latency"] = decode_latency()
     if not args.no_cpu_baseline:
@@ -291,6 +294,35 @@ def decode_latency(n=200):
     res["fused_us"] = res["route_dispatch_fused_us"] + res["combine_us"]
     res["workload"] = f"decode: {wl.description}"
     return res
+
+
+def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, iters=5):
+    """The W8A8 expert layer (hidden -> hidden per physical expert) over the
+    global batch's occupied slots, against the int8 MFMA roofline."""
+    import torch
+    H, P = wl.hidden, wl.num_phys
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    Wd = torch.randint(-127, 128, (P, H, H), dtype=torch.int8, device="cuda", generator=gen)
+    wsd = (torch.rand((P, H), device="cuda", generator=gen) + 0.5) / (127.0 * H ** 0.5)
+    used = torch.minimum(counts, torch.from_numpy(wl.capacity).cuda()).sum().item()
+    plan.expert_w8a8(counts, dbuf, Wd, wsd, cbuf, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        plan.expert_w8a8(counts, dbuf, Wd, wsd, cbuf, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / iters
+    ops = 2.0 * used * H * H
+    del Wd
+    torch.cuda.empty_cache()
+    return {"kernel": "expert_w8a8", "us": us, "rows": int(used),
+            "TOPs": ops / (us * 1e-6) / 1e12,
+            "roofline": {"bound": "mfma", "achieved": ops / (us * 1e-6) / 1e12,
+                         "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
+                         "frac": ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS},
+            "weight_GBps": P * H * H / (us * 1e-6) / 1e9}
 
 
 def calib_copy(args):
@@ -389,6 +421,7 @@ def main():
     ap.add_argument("--combine-fmt", choices=["bf16", "q8"], default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-expert", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--calib-copy", action="store_true")

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoedc.so")
-SOURCES = ["route.hip", "dispatch.hip", "fused.hip", "combine.hip", "stub.hip", "host.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "fused.hip", "combine.hip", "stub.hip",
+           "expert_gemm.hip", "host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

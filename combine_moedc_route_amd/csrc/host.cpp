@@ -129,6 +129,7 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
     w.rep_count = o;     o = round_up(o + 4 * (int64_t)E, kWsAlign);
     w.rep_table = o;     o = round_up(o + 4 * (int64_t)E * R, kWsAlign);
     w.block_counts = o;  o = round_up(o + 4 * (int64_t)p->nblk_max * P, kWsAlign);
+    w.tile_base = o;     o = round_up(o + 4 * (int64_t)(P + 1), kWsAlign);
     w.bytes = o;
   } catch (...) {
     delete p;
@@ -324,6 +325,31 @@ moedc_status moedc_combine_limited(const moedc_plan *p, int32_t T, const void *e
                                    const int32_t *slots, const float *topk_w, uint16_t *y,
                                    int32_t max_workgroups, hipStream_t stream) {
   return combine_impl(p, T, eout, fmt, slots, topk_w, y, max_workgroups, stream);
+}
+
+moedc_status moedc_expert_w8a8(const moedc_plan *p, const int32_t *counts, const void *dbuf,
+                               const int8_t *weights, const float *w_scale,
+                               uint16_t *ebuf, void *ws, hipStream_t stream) {
+  if (!p || !counts || !dbuf || !weights || !w_scale || !ebuf || !ws) return MOEDC_ERR_INVALID_ARG;
+  if (!aligned16(dbuf) || !aligned16(weights) || !aligned16(w_scale) || !aligned16(ebuf) ||
+      !aligned16(ws) || !aligned4(counts))
+    return MOEDC_ERR_ALIGN;
+  moedc::GemmArgs a{};
+  a.dbuf = static_cast<const uint8_t *>(dbuf);
+  a.W = weights;
+  a.w_scale = w_scale;
+  a.ebuf = ebuf;
+  a.counts = counts;
+  a.cap = ws_ptr<const int32_t>(ws, p->ws.cap);
+  a.capbase = ws_ptr<const int32_t>(ws, p->ws.capbase);
+  a.tile_base = ws_ptr<int32_t>(ws, p->ws.tile_base);
+  a.slot_stride = p->slot_stride;
+  a.H = p->cfg.hidden;
+  a.P = p->cfg.num_phys_experts;
+  a.ntiles = p->cfg.hidden / 128;
+  a.steps_per_group = p->cfg.group_size / 128;
+  const hipError_t e = moedc::launch_expert_gemm(a, 2048, stream);
+  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }
 
 moedc_status moedc_expert_stub(const moedc_plan *p, const int32_t *counts, const void *dbuf,

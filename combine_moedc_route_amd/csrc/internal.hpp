@@ -29,6 +29,7 @@ struct WsLayout {
   int64_t rep_count = 0;    // int32 [E]
   int64_t rep_table = 0;    // int32 [E][R]
   int64_t block_counts = 0; // int32 [nblk_max][P]
+  int64_t tile_base = 0;    // int32 [P+1]: expert GEMM work list
   int64_t bytes = 0;
 };
 
@@ -81,12 +82,26 @@ struct StubArgs {
   int32_t per_token;
 };
 
+struct GemmArgs {
+  const uint8_t *dbuf;
+  const int8_t *W;
+  const float *w_scale;
+  uint16_t *ebuf;
+  const int32_t *counts;
+  const int32_t *cap;
+  const int32_t *capbase;
+  int32_t *tile_base;
+  int64_t slot_stride;
+  int32_t H, P, ntiles, steps_per_group;
+};
+
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_stub(const StubArgs &a, hipStream_t s);
 hipError_t launch_route_dispatch_fused(const RouteArgs &ra, const DispatchArgs &da,
                                        hipStream_t s);
+hipError_t launch_expert_gemm(const GemmArgs &a, int grid, hipStream_t s);
 
 }  // namespace moedc
 

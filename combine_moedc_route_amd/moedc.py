@@ -25,7 +25,8 @@ EXPORTS = (
     "moedc_plan_create", "moedc_plan_destroy", "moedc_plan_sizes",
     "moedc_plan_bind_workspace", "moedc_route", "moedc_dispatch",
     "moedc_combine", "moedc_route_dispatch", "moedc_combine_limited",
-    "moedc_expert_stub", "moedc_status_string", "moedc_last_hip_error",
+    "moedc_expert_stub", "moedc_expert_w8a8", "moedc_status_string",
+    "moedc_last_hip_error",
 )
 
 
@@ -108,6 +109,8 @@ def load_library(path):
     L.moedc_route_dispatch.restype = i32
     L.moedc_combine_limited.argtypes = [P, i32, P, i32, P, P, P, i32, P]
     L.moedc_combine_limited.restype = i32
+    L.moedc_expert_w8a8.argtypes = [P, P, P, P, P, P, P, P]
+    L.moedc_expert_w8a8.restype = i32
     L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
     L.moedc_expert_stub.restype = i32
     L.moedc_status_string.argtypes = [i32]
@@ -249,6 +252,12 @@ class Plan:
         _check(lib().moedc_combine_limited(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
                                            _ptr(topk_w), _ptr(y), max_workgroups,
                                            _stream(stream)), "moedc_combine_limited")
+
+    def expert_w8a8(self, counts, dispatch_buf, weights, w_scale, combine_buf, workspace,
+                    stream=None):
+        _check(lib().moedc_expert_w8a8(self._h, _ptr(counts), _ptr(dispatch_buf), _ptr(weights),
+                                       _ptr(w_scale), _ptr(combine_buf), _ptr(workspace),
+                                       _stream(stream)), "moedc_expert_w8a8")
 
     def expert_stub(self, counts, dispatch_buf, combine_buf, workspace, stream=None):
         _check(lib().moedc_expert_stub(self._h, _ptr(counts), _ptr(dispatch_buf),

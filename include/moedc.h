@@ -225,6 +225,27 @@ moedc_status moedc_expert_stub(const moedc_plan *plan, const int32_t *counts,
                                const void *dispatch_buf, uint16_t *combine_buf,
                                void *workspace, hipStream_t stream);
 
+/*
+ * Expert compute between dispatch and combine: one W8A8 linear layer per
+ * physical expert (hidden -> hidden), the INT8 matmul of "INT8
+ * Quantization" (CloudMatrix384 article: per-token dynamic activation
+ * scales, per-channel static weight scales).  For every occupied slot row t
+ * of expert p (the first min(counts[p], capacity[p]) slots of its window)
+ * and output channel n:
+ *   isum_g = sum over scale group g of q[t][k] * weights[p][n][k]  (int32)
+ *   acc = +0; acc = fmaf(s_x[t][g], (float)isum_g, acc), g ascending
+ *   combine_buf[t][n] = BF16 round-to-nearest-even of acc * w_scale[p][n]
+ * reading q and s_x in place from dispatch_buf.  weights: int8
+ * [E_phys][H][H] (row n = output channel); w_scale: fp32 [E_phys][H];
+ * combine_buf: BF16 [total_slots][H]; all 16-byte aligned.  Other rows of
+ * combine_buf are not written.  Runs on int8 MFMA.
+ * Errors: INVALID_ARG, ALIGN, HIP.
+ */
+moedc_status moedc_expert_w8a8(const moedc_plan *plan, const int32_t *counts,
+                               const void *dispatch_buf, const int8_t *weights,
+                               const float *w_scale, uint16_t *combine_buf,
+                               void *workspace, hipStream_t stream);
+
 /* Static English text for a status code. */
 const char *moedc_status_string(moedc_status status);
 

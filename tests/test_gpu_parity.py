@@ -355,3 +355,65 @@ def test_combine_limited_matches_combine(workgroups, fmt):
     y = torch.full((x.shape[0], wl.hidden), -1, dtype=torch.int16, device="cuda")
     plan.combine_limited(src, fmt, dev(r["slots"]), dev(r["topk_w"]), y, workgroups)
     assert np.array_equal(host_u16(y), want)
+
+
+# ------------------------------------------------------------------ expert W8A8 GEMM
+
+def _gemm_case(wl, x, logits, seed=21):
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    s = plan.sizes
+    r = oracle.route(cfg, logits)
+    dref = oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride)
+    Wt, ws = W.make_expert_weights(seed, wl.num_phys, wl.hidden)
+    want = oracle.expert_w8a8(cfg, r["counts"], dref, s.slot_stride, Wt, ws,
+                              ebuf=np.full((s.total_slots, wl.hidden), 0x7FC1, np.uint16))
+    wsp = torch.empty(s.workspace_bytes, dtype=torch.uint8, device="cuda")
+    plan.bind_workspace(wsp)
+    out = torch.full((s.total_slots, wl.hidden), 0x7FC1, dtype=torch.int16, device="cuda")
+    plan.expert_w8a8(dev(r["counts"]), dev(dref), torch.from_numpy(Wt).cuda(), dev(ws), out, wsp)
+    got = host_u16(out)
+    assert np.array_equal(got, want), f"{(got != want).any(axis=1).sum()} rows differ"
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "overflow", "replica_shared"])
+def test_expert_w8a8_parity(name):
+    wl, x, logits, plan, cfg = setup(name)
+    _gemm_case(wl, x, logits)
+
+
+@pytest.mark.parametrize("H,T", [(1024, 150), (2048, 70)])
+def test_expert_w8a8_parity_per_token(H, T):
+    wl = W.Workload("pt", "", T, H, 8, 8, 3, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(8, T, np.int32), None, 31, "normal", ("fraction", 0.05, 50.0),
+                    group_size=H)
+    log(f"[case] expert gemm per-token H={H} T={T}")
+    x, logits = W.make_inputs(wl)
+    _gemm_case(wl, x, logits)
+
+
+def test_expert_w8a8_full_size_sampled():
+    wl, x, logits, plan, cfg = setup("global")
+    s = plan.sizes
+    H, P = wl.hidden, wl.num_phys
+    r = oracle.route(cfg, logits)
+    b = plan.alloc()
+    plan.dispatch(dev_i16(x), dev(r["slots"]), b["dispatch_buf"])
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    Wd = torch.randint(-127, 128, (P, H, H), dtype=torch.int8, device="cuda", generator=gen)
+    wsd = (torch.rand((P, H), device="cuda", generator=gen) + 0.5) / (127.0 * H ** 0.5)
+    plan.expert_w8a8(dev(r["counts"]), b["dispatch_buf"], Wd, wsd, b["combine_buf"],
+                     b["workspace"])
+    torch.cuda.synchronize()
+    dview = b["dispatch_buf"].view(s.total_slots, s.slot_stride)
+    base = np.concatenate([[0], np.cumsum(wl.capacity)[:-1]])
+    for p in (0, 77, 200, 255):
+        n_p = min(int(r["counts"][p]), int(wl.capacity[p]))
+        rows = np.unique(np.concatenate([[0, n_p - 1], np.arange(0, n_p, 97)]))
+        sl = base[p] + rows
+        d = dview[torch.from_numpy(sl).cuda()].cpu().numpy()
+        one = oracle.Cfg(H, 1, 1, 1, 0, 1, [len(rows)], group_size=wl.group_size)
+        want = oracle.expert_w8a8(one, np.array([len(rows)], np.int32), d, s.slot_stride,
+                                  Wd[p:p + 1].cpu().numpy(), wsd[p:p + 1].cpu().numpy())
+        got = host_u16(b["combine_buf"][torch.from_numpy(sl).cuda()])
+        assert np.array_equal(got, want), p
