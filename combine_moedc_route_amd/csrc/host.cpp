@@ -346,9 +346,9 @@ moedc_status moedc_expert_w8a8(const moedc_plan *p, const int32_t *counts, const
   a.slot_stride = p->slot_stride;
   a.H = p->cfg.hidden;
   a.P = p->cfg.num_phys_experts;
-  a.ntiles = p->cfg.hidden / 128;
+  a.ntiles = (p->cfg.hidden + 255) / 256;
   a.steps_per_group = p->cfg.group_size / 128;
-  const hipError_t e = moedc::launch_expert_gemm(a, 2048, stream);
+  const hipError_t e = moedc::launch_expert_gemm(a, 256, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }
 
