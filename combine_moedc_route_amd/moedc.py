@@ -25,8 +25,8 @@ EXPORTS = (
     "moedc_plan_create", "moedc_plan_destroy", "moedc_plan_sizes",
     "moedc_plan_bind_workspace", "moedc_route", "moedc_dispatch",
     "moedc_combine", "moedc_route_dispatch", "moedc_combine_limited",
-    "moedc_expert_stub", "moedc_expert_w8a8", "moedc_status_string",
-    "moedc_last_hip_error",
+    "moedc_expert_stub", "moedc_expert_w8a8", "moedc_place_replicas",
+    "moedc_lpt_partition", "moedc_status_string", "moedc_last_hip_error",
 )
 
 
@@ -113,6 +113,10 @@ def load_library(path):
     L.moedc_expert_w8a8.restype = i32
     L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
     L.moedc_expert_stub.restype = i32
+    L.moedc_place_replicas.argtypes = [i32, P, i32, i32, P]
+    L.moedc_place_replicas.restype = i32
+    L.moedc_lpt_partition.argtypes = [i32, P, P, i32, i32, i32, P, C.POINTER(C.c_double)]
+    L.moedc_lpt_partition.restype = i32
     L.moedc_status_string.argtypes = [i32]
     L.moedc_status_string.restype = C.c_char_p
     L.moedc_last_hip_error.argtypes = []
@@ -144,6 +148,31 @@ def _stream(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def place_replicas(load, num_redundant: int, max_replicas: int) -> np.ndarray:
+    """Replica table [E][max_replicas] from expected per-expert loads."""
+    load = np.ascontiguousarray(load, dtype=np.float64)
+    table = np.empty((load.size, max_replicas), np.int32)
+    _check(lib().moedc_place_replicas(load.size, load.ctypes.data_as(C.c_void_p), num_redundant,
+                                      max_replicas, table.ctypes.data_as(C.c_void_p)),
+           "moedc_place_replicas")
+    return table
+
+
+def lpt_partition(cost, num_workers: int, group=None, num_groups: int = 0,
+                  fanout_cap: int = 0):
+    """(assign [U] int32, makespan) of the LPT list schedule."""
+    cost = np.ascontiguousarray(cost, dtype=np.float64)
+    g = None if group is None else np.ascontiguousarray(group, dtype=np.int32)
+    assign = np.empty(cost.size, np.int32)
+    ms = C.c_double()
+    _check(lib().moedc_lpt_partition(cost.size, cost.ctypes.data_as(C.c_void_p),
+                                     None if g is None else g.ctypes.data_as(C.c_void_p),
+                                     num_groups, num_workers, fanout_cap,
+                                     assign.ctypes.data_as(C.c_void_p), C.byref(ms)),
+           "moedc_lpt_partition")
+    return assign, ms.value
 
 
 class Plan:

@@ -246,6 +246,42 @@ moedc_status moedc_expert_w8a8(const moedc_plan *plan, const int32_t *counts,
                                const float *w_scale, uint16_t *combine_buf,
                                void *workspace, hipStream_t stream);
 
+/*
+ * Load-proportional placement of redundant experts ("Decode Phase" of the
+ * CloudMatrix384 article: redundant copies of experts balance load).  Given
+ * the expected load of each logical expert (>= 0, e.g. the previous batch's
+ * counts), assigns num_redundant extra copies, each to the expert with the
+ * largest load per copy (ties to the lower id) below max_replicas copies,
+ * which minimises the largest load per physical expert.  Writes
+ * replica_table [num_logical][max_replicas] in the layout moedc_config
+ * takes: row e = e, then the physical ids num_logical, num_logical+1, ...
+ * of its extra copies in the order they were assigned, then -1.
+ * Host memory only; no device work.
+ * Errors: INVALID_ARG (negative or non-finite load, more copies than
+ * num_logical * (max_replicas - 1), NULL pointers).
+ */
+moedc_status moedc_place_replicas(int32_t num_logical, const double *load,
+                                  int32_t num_redundant, int32_t max_replicas,
+                                  int32_t *replica_table);
+
+/*
+ * Workload-balanced partitioning of expert-major work units over workers
+ * ("StrataCL 深度技术分析", section 3.5: minimise the largest per-core
+ * load under a per-peer fan-out cap, by an LPT list scheduler).  Units are
+ * taken longest first (equal costs in index order); each goes to the least
+ * loaded worker (ties to the lower index) among those allowed: when
+ * fanout_cap > 0, a group already served by fanout_cap workers may only be
+ * given to one of those.  assign[u] receives the worker of unit u,
+ * *makespan the largest worker load.  Without a cap the makespan is at most
+ * (4/3 - 1/(3 * num_workers)) times the optimum.  O(U log U + U * W) on the
+ * host; no device work.
+ * Errors: INVALID_ARG (negative or non-finite cost, group outside
+ * [0, num_groups) when capped, NULL pointers).
+ */
+moedc_status moedc_lpt_partition(int32_t num_units, const double *cost, const int32_t *group,
+                                 int32_t num_groups, int32_t num_workers, int32_t fanout_cap,
+                                 int32_t *assign, double *makespan);
+
 /* Static English text for a status code. */
 const char *moedc_status_string(moedc_status status);
 

@@ -417,3 +417,25 @@ def test_expert_w8a8_full_size_sampled():
                                   Wd[p:p + 1].cpu().numpy(), wsd[p:p + 1].cpu().numpy())
         got = host_u16(b["combine_buf"][torch.from_numpy(sl).cuda()])
         assert np.array_equal(got, want), p
+
+
+def test_route_eight_copy_replicas():
+    """Replica rows of up to 8 copies (the layout the load-proportional
+    placement produces), on the skewed logits."""
+    base = W.get("skewed")
+    E, R = base.num_logical, 8
+    table = np.full((E, R), -1, np.int32)
+    table[:, 0] = np.arange(E)
+    nxt = E
+    for e, copies in ((0, 8), (1, 4), (2, 3), (3, 2), (5, 2)):
+        for c in range(1, copies):
+            table[e, c] = nxt
+            nxt += 1
+    P = nxt
+    wl = W.Workload("rep8", "", 3000, 256, E, P, 8, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(P, 3000, np.int32), table, base.seed, "zipf")
+    log(f"[case] 8-copy replicas P={P}")
+    x, logits = W.make_inputs(wl)
+    want = oracle.route(oracle.Cfg.from_workload(wl), logits)
+    compare_route(wl, gpu_route(M.Plan.from_workload(wl), wl, logits)[0], want)
+    assert (np.bincount(want["topk_ids"].ravel(), minlength=P)[E:] > 0).all()
