@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "combine": "combine_moedc_route_amd/csrc/combine.hip",
     "dispatch": "combine_moedc_route_amd/csrc/dispatch.hip",
     "route": "combine_moedc_route_amd/csrc/route.hip",
+    "expert_gemm": "combine_moedc_route_amd/csrc/expert_gemm.hip",
 }
 
 
@@ -321,7 +322,8 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, iters=5):
             "TOPs": ops / (us * 1e-6) / 1e12,
             "roofline": {"bound": "mfma", "achieved": ops / (us * 1e-6) / 1e12,
                          "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
-                         "frac": ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS},
+                         "frac": ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS,
+                         "traffic": measured_traffic("expert_gemm")},
             "weight_GBps": P * H * H / (us * 1e-6) / 1e9}
 
 
@@ -398,8 +400,8 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
                      f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
                      f"{copy_bytes}-byte copy); valid while source_sha matches."}
-    for key, tag in (("combine", "combine_kernel<8, false>"), ("dispatch", "dispatch_kernel<14>"),
-                     ("route", "route_topk_rank<8, false>")):
+    for key, tag in (("combine", "combine_kernel<8, false>"), ("dispatch", "dispatch_kernel<14, false>"),
+                     ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm(")):
         kf = [k for k in fetch if tag in k]
         kw = [k for k in write if tag in k]
         if not kf or not kw:
