@@ -14,17 +14,25 @@
 //   y[t][n] = bf16(acc * w_scale[p][n])
 // (a group is 128 inputs, or the whole row with one scale per token).
 //
-// Work list: gemm_tiles turns the route's counts into tiles of 128 slot rows
-// x 256 channels, expert-major; a persistent grid walks the list.  Per tile,
-// 8 waves (2 token halves x 4 channel quarters, 64 x 64 each); MFMA
+// Work list: the route's counts give each expert ceil(rows/128) row tiles
+// and ceil(H/256) channel tiles.  A band is kBandTiles channel tiles x all
+// row tiles of one expert (32 tiles for 8 row tiles), ordered row-major so
+// that neighbouring entries share a weight slice or a slot tile.  Bands are
+// dealt round-robin to the 8 XCDs; workgroup b runs on XCD b mod 8 (the
+// hardware's round-robin placement), and the 32 workgroups resident on one
+// XCD walk that XCD's band stream together.  The tiles of a band then run
+// concurrently on one die, so each 256-channel weight slice and each slot
+// tile crosses from memory into that die's L2 about once per band instead
+// of once per tile.  The placement is only a performance assumption: any
+// placement computes the same result.
+//
+// Per tile, 8 waves (2 token halves x 4 channel quarters, 64 x 64 each); MFMA
 // v_mfma_i32_16x16x64_i8 with A = 16 weight rows (channels) and B = 16 slot
 // rows (tokens), so each lane ends up with 4 consecutive channels of one
 // token (8-byte BF16 stores).  K advances 128 inputs per step; slot rows and
 // weight rows are shared by 4 and 2 waves respectively and pass through a
 // double-buffered LDS tile, loaded one step ahead into registers, with one
-// barrier per step.  A tile moves 48 KiB per step for 8.4 MOP (175 op/B),
-// twice the reuse of a 64 x 128 tile: the kernel is bound by cache
-// bandwidth before MFMA throughput.
+// barrier per step.  A tile moves 48 KiB per step for 8.4 MOP (175 op/B).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -35,34 +43,47 @@ namespace moedc {
 namespace {
 
 constexpr int BM = 128;   // slot rows (tokens) per tile
-constexpr int BN = 256;   // output channels per tile
+constexpr int BN = kGemmChannels;  // output channels per tile
 constexpr int BK = 128;   // inputs per K step
-constexpr int PITCH = BK + 16;  // LDS row pitch: conflict-free 16-byte reads
+
+// LDS tiles are unpadded rows of BK bytes; the 16-byte chunk c of row r is
+// stored at chunk c ^ (r & 7).  The 16-byte fragment reads (16 rows, one
+// chunk) and the staging writes (8 chunks of one row) then hit distinct
+// banks, and the tiles need no padding.
+__device__ __forceinline__ int swz(int r, int chunk) { return 16 * (chunk ^ (r & 7)); }
 constexpr int kThreads = 512;   // 8 waves: 2 token halves x 4 channel quarters
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// counts -> tile_base[p] = tiles of experts < p; tile_base[P] = total.
+// counts -> band_pre[x][j]: tiles in the bands x, x+8, ..., x+8(j-1) dealt
+// to XCD x (band k = expert k / nbe, channel tiles kBandTiles (k mod nbe) on);
+// band_pre[x][J] is XCD x's total.  J <= 1024 (P <= 1024, nbe <= 8).
 __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
   __shared__ int wsum[16];
-  const int tid = threadIdx.x;
-  int tiles = 0;
-  if (tid < a.P) {
-    const int used = min(a.counts[tid], a.cap[tid]);
-    tiles = (used + BM - 1) / BM * a.ntiles;
-  }
-  int incl = tiles;
+  const int j = threadIdx.x;
+  for (int x = 0; x < kXcds; ++x) {
+    const int k = x + kXcds * j;
+    int tiles = 0;
+    if (j < a.J && k < a.P * a.nbe) {
+      const int p = k / a.nbe, b = k % a.nbe;
+      const int rows = min(a.counts[p], a.cap[p]);
+      tiles = (rows + BM - 1) / BM * min(kBandTiles, a.ntiles - b * kBandTiles);
+    }
+    int incl = tiles;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(incl, d);
-    if ((tid & 63) >= d) incl += u;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if ((j & 63) >= d) incl += u;
+    }
+    if ((j & 63) == 63) wsum[j >> 6] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < (j >> 6); ++w) base += wsum[w];
+    int32_t *row = a.band_pre + x * (a.J + 1);
+    if (j < a.J) row[j] = base + incl - tiles;
+    if (j == a.J - 1) row[a.J] = base + incl;
+    __syncthreads();  // wsum is reused by the next XCD's scan
   }
-  if ((tid & 63) == 63) wsum[tid >> 6] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
-  if (tid < a.P) a.tile_base[tid] = base + incl - tiles;
-  if (tid == a.P - 1) a.tile_base[a.P] = base + incl;
 }
 
 // Loads of K step g: 16 KiB of weights (4 x 16 B per thread, rows n, n+32,
@@ -106,20 +127,24 @@ __device__ __forceinline__ StepRegs fetch_step(const GemmArgs &a, const int8_t *
 // Scales are double-buffered by group parity: group j's scale is written
 // with its first step and read after its last, while group j+1's goes to
 // the other buffer.
-__device__ __forceinline__ void stage(int8_t (&Xs)[BM][PITCH], int8_t (&Ws)[BN][PITCH],
+__device__ __forceinline__ void stage(int8_t (&Xs)[BM][BK], int8_t (&Ws)[BN][BK],
                                       float (&sx)[2][BM], const StepRegs &st, int g, int spg,
                                       int tid) {
-  const int r = tid >> 3, c = 16 * (tid & 7);
+  const int r = tid >> 3, c = tid & 7;  // rows r + 64 i keep r's low 3 bits
 #pragma unroll
-  for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][c]) = st.x[i];
+  for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][swz(r, c)]) = st.x[i];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i *>(&Ws[r + 64 * i][c]) = st.w[i];
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i *>(&Ws[r + 64 * i][swz(r, c)]) = st.w[i];
   if (tid < BM && g % spg == 0) sx[(g / spg) & 1][tid] = st.s;
 }
 
+// G128: every K step is one 128-input scale group, so the first MFMA of a
+// step starts from a zero accumulator and the group's int32 sums are folded
+// into fp32 at the end of the same step.  Otherwise one scale spans the row.
+template <bool G128>
 __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BM][PITCH];
-  __shared__ __attribute__((aligned(16))) int8_t Ws[2][BN][PITCH];
+  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BM][BK];
+  __shared__ __attribute__((aligned(16))) int8_t Ws[2][BN][BK];
   __shared__ float sx[2][BM];
 
   const int tid = threadIdx.x;
@@ -128,19 +153,24 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
   const int wm = wave & 1, wn = wave >> 1;  // token half, channel quarter
   const int H = a.H;
   const int ksteps = H / BK;
-  const int spg = a.steps_per_group;  // K steps per activation scale
-  const int total = uniform(a.tile_base[a.P]);
+  const int spg = G128 ? 1 : a.steps_per_group;  // K steps per activation scale
+  const int xcd = blockIdx.x % kXcds;
+  const int nblk = gridDim.x / kXcds;  // workgroups sharing this XCD's stream
+  const int32_t *row = a.band_pre + xcd * (a.J + 1);
+  const int total = uniform(row[a.J]);
 
-  for (int lin = blockIdx.x; lin < total; lin += gridDim.x) {
-    // ---- locate the tile: expert p owns tile_base[p] .. tile_base[p+1) ----
-    int lo = 0, hi = a.P;
+  for (int q = blockIdx.x / kXcds; q < total; q += nblk) {
+    // ---- locate the tile: band j of this XCD holds row[j] .. row[j+1) ----
+    int lo = 0, hi = a.J;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (a.tile_base[mid] <= lin) lo = mid; else hi = mid;
+      if (row[mid] <= q) lo = mid; else hi = mid;
     }
-    const int p = uniform(lo);
-    const int r = lin - a.tile_base[p];
-    const int mt = r / a.ntiles, nt = r % a.ntiles;
+    const int k = uniform(xcd + kXcds * lo);
+    const int p = k / a.nbe, band = k % a.nbe;
+    const int off = q - row[lo];
+    const int w = min(kBandTiles, a.ntiles - band * kBandTiles);
+    const int mt = off / w, nt = band * kBandTiles + off % w;
     const int used = min(a.counts[p], a.cap[p]);
     const int rows = min(BM, used - mt * BM);
     const int chans = min(BN, H - nt * BN);
@@ -171,17 +201,17 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf)
           av[nf] = *reinterpret_cast<const v4i *>(
-              &Ws[buf][64 * wn + 16 * nf + (lane & 15)][64 * kk + 16 * (lane >> 4)]);
+              &Ws[buf][64 * wn + 16 * nf + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf)
           bv[tf] = *reinterpret_cast<const v4i *>(
-              &Xs[buf][64 * wm + 16 * tf + (lane & 15)][64 * kk + 16 * (lane >> 4)]);
+              &Xs[buf][64 * wm + 16 * tf + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
           for (int tf = 0; tf < 4; ++tf)
-            acc[nf][tf] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(av[nf], bv[tf], acc[nf][tf], 0, 0, 0);
+            acc[nf][tf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                av[nf], bv[tf], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][tf], 0, 0, 0);
       }
       if (g + 1 < ksteps) stage(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
       if (g + 2 < ksteps) nxt = fetch_step(a, wtile, slot0, rows, chans, g + 2, spg, tid);
@@ -195,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               accf[nf][tf][q] = __builtin_fmaf(s, (float)acc[nf][tf][q], accf[nf][tf][q]);
-            acc[nf][tf] = v4i{0, 0, 0, 0};
+            if (!G128) acc[nf][tf] = v4i{0, 0, 0, 0};
           }
         }
       }
@@ -224,10 +254,14 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_expert_gemm(const GemmArgs &a, int grid, hipStream_t s) {
+  if (a.J > 1024 || grid % kXcds) return hipErrorInvalidValue;
   gemm_tiles<<<1, 1024, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  expert_gemm<<<grid, kThreads, 0, s>>>(a);
+  if (a.steps_per_group == 1)
+    expert_gemm<true><<<grid, kThreads, 0, s>>>(a);
+  else
+    expert_gemm<false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

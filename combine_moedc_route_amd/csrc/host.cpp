@@ -129,7 +129,10 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
     w.rep_count = o;     o = round_up(o + 4 * (int64_t)E, kWsAlign);
     w.rep_table = o;     o = round_up(o + 4 * (int64_t)E * R, kWsAlign);
     w.block_counts = o;  o = round_up(o + 4 * (int64_t)p->nblk_max * P, kWsAlign);
-    w.tile_base = o;     o = round_up(o + 4 * (int64_t)(P + 1), kWsAlign);
+    const int32_t ntiles = (c.hidden + kGemmChannels - 1) / kGemmChannels;
+    p->gemm_nbe = (ntiles + kBandTiles - 1) / kBandTiles;
+    p->gemm_J = (int32_t)(((int64_t)P * p->gemm_nbe + kXcds - 1) / kXcds);
+    w.band_pre = o;      o = round_up(o + 4 * (int64_t)kXcds * (p->gemm_J + 1), kWsAlign);
     w.bytes = o;
   } catch (...) {
     delete p;
@@ -342,13 +345,16 @@ moedc_status moedc_expert_w8a8(const moedc_plan *p, const int32_t *counts, const
   a.counts = counts;
   a.cap = ws_ptr<const int32_t>(ws, p->ws.cap);
   a.capbase = ws_ptr<const int32_t>(ws, p->ws.capbase);
-  a.tile_base = ws_ptr<int32_t>(ws, p->ws.tile_base);
+  a.band_pre = ws_ptr<int32_t>(ws, p->ws.band_pre);
   a.slot_stride = p->slot_stride;
   a.H = p->cfg.hidden;
   a.P = p->cfg.num_phys_experts;
-  a.ntiles = (p->cfg.hidden + 255) / 256;
+  a.ntiles = (p->cfg.hidden + moedc::kGemmChannels - 1) / moedc::kGemmChannels;
   a.steps_per_group = p->cfg.group_size / 128;
-  const hipError_t e = moedc::launch_expert_gemm(a, 256, stream);
+  a.nbe = p->gemm_nbe;
+  a.J = p->gemm_J;
+  // One persistent workgroup per CU: 32 on each of the 8 XCDs.
+  const hipError_t e = moedc::launch_expert_gemm(a, 32 * moedc::kXcds, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }
 

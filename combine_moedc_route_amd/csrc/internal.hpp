@@ -21,6 +21,11 @@ constexpr int kRouteTokens = 64;     // tokens per route block (4 lanes per toke
 constexpr int kFusedMaxTokens = 256; // largest batch of the single-launch route + dispatch
 constexpr int64_t kSlotAlign = 512;  // dispatch slot stride granularity
 constexpr int64_t kWsAlign = 256;
+// Expert GEMM work list: bands of kBandTiles channel tiles x all row tiles
+// of one expert, dealt round-robin to the kXcds accelerator dies.
+constexpr int kXcds = 8;
+constexpr int kBandTiles = 4;
+constexpr int kGemmChannels = 256;  // output channels per tile
 
 // Workspace byte offsets (all kWsAlign-aligned).
 struct WsLayout {
@@ -29,7 +34,7 @@ struct WsLayout {
   int64_t rep_count = 0;    // int32 [E]
   int64_t rep_table = 0;    // int32 [E][R]
   int64_t block_counts = 0; // int32 [nblk_max][P]
-  int64_t tile_base = 0;    // int32 [P+1]: expert GEMM work list
+  int64_t band_pre = 0;     // int32 [8][gemm_J+1]: expert GEMM work list per XCD
   int64_t bytes = 0;
 };
 
@@ -90,9 +95,11 @@ struct GemmArgs {
   const int32_t *counts;
   const int32_t *cap;
   const int32_t *capbase;
-  int32_t *tile_base;
+  int32_t *band_pre;        // [kXcds][J+1] exclusive tile prefix of each XCD's bands
   int64_t slot_stride;
   int32_t H, P, ntiles, steps_per_group;
+  int32_t nbe;              // bands per expert: ceil(ntiles / kBandTiles)
+  int32_t J;                // bands per XCD: ceil(P * nbe / kXcds)
 };
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
@@ -109,6 +116,7 @@ struct moedc_plan {
   moedc_config cfg;                 // pointer fields point into the vectors below
   std::vector<int32_t> cap, capbase, rep_count, rep_table;
   int32_t K, G, nblk_max;
+  int32_t gemm_nbe, gemm_J;         // expert GEMM bands per expert / per XCD
   int64_t slot_stride, combine_stride, total_slots;
   moedc::WsLayout ws;
 };
