@@ -71,39 +71,65 @@ def measured_traffic(kernel):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(tokens=16384):
-    """The oracle, single-threaded, on a bounded sample of the same workload:
-    `tokens` tokens drawn with the same recipe and seed, per-expert capacity
-    scaled to 2x their mean load.  Times route + dispatch + combine (the stand-in expert is untimed,
-    as on the GPU)."""
+def cpu_baseline(tokens=30720, reps=3):
+    """The oracle, single-threaded and pinned to one host core, on the same
+    workload recipe (`tokens` tokens, seed and capacity as on the GPU when
+    tokens = 30720).  Route, dispatch and combine are each timed `reps`
+    times and the per-step medians summed; the stand-in expert fills the
+    combine buffer once, untimed, as on the GPU."""
     import numpy as np
 
     import oracle
     from combine_moedc_route_amd import workloads as W
     wl = W.get("global")
-    cap = 2 * tokens * wl.K // wl.num_phys
-    sub = W.Workload("global-prefix", "", tokens, wl.hidden, wl.num_logical, wl.num_phys,
-                     wl.top_k, 0, wl.score_fn, np.full(wl.num_phys, cap, np.int32), None,
-                     wl.seed, wl.logits_kind)
+    if tokens == wl.tokens:
+        sub = wl
+    else:
+        cap = 2 * tokens * wl.K // wl.num_phys
+        sub = W.Workload("global-prefix", "", tokens, wl.hidden, wl.num_logical, wl.num_phys,
+                         wl.top_k, 0, wl.score_fn, np.full(wl.num_phys, cap, np.int32), None,
+                         wl.seed, wl.logits_kind)
     x, logits = W.make_inputs(sub)
     cfg = oracle.Cfg.from_workload(sub)
-    H, G = wl.hidden, wl.hidden // 128
+    H, G = sub.hidden, sub.hidden // 128
     sd = -(-(H + 4 * G) // 512) * 512
-    S = cap * wl.num_phys
-    t0 = time.perf_counter()
-    r = oracle.route(cfg, logits)
-    t1 = time.perf_counter()
-    dbuf = oracle.dispatch(cfg, x, r["slots"], S, sd)
-    t2 = time.perf_counter()
-    ebuf = oracle.expert_stub(cfg, r["counts"], dbuf, sd)
-    t3 = time.perf_counter()
-    oracle.combine(cfg, ebuf, oracle.FMT_BF16, r["slots"], r["topk_w"])
-    t4 = time.perf_counter()
-    sec = (t1 - t0) + (t2 - t1) + (t4 - t3)
+    S = int(np.sum(sub.capacity))
+    # Buffers are allocated and touched before timing, as the GPU's are
+    # resident before its timed region (first-touch page faults excluded).
+    dbuf = np.zeros((S, sd), np.uint8)
+    dbuf.fill(0)
+    y = np.empty((tokens, H), np.uint16)
+    y.fill(0)
+    old = os.sched_getaffinity(0)
+    core = min(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        t_r, t_d, t_c = [], [], []
+        ebuf = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            r = oracle.route(cfg, logits)
+            t1 = time.perf_counter()
+            oracle.dispatch(cfg, x, r["slots"], S, sd, buf=dbuf)
+            t2 = time.perf_counter()
+            if ebuf is None:
+                ebuf = oracle.expert_stub(cfg, r["counts"], dbuf, sd)  # writes every row combine reads
+            t3 = time.perf_counter()
+            oracle.combine(cfg, ebuf, oracle.FMT_BF16, r["slots"], r["topk_w"], out=y)
+            t4 = time.perf_counter()
+            t_r.append(t1 - t0)
+            t_d.append(t2 - t1)
+            t_c.append(t4 - t3)
+    finally:
+        os.sched_setaffinity(0, old)
+    med = [statistics.median(v) for v in (t_r, t_d, t_c)]
+    sec = sum(med)
     return {"value": tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{tokens} tokens of the 30720-token workload recipe, capacity {cap}/expert; "
-                      f"route {1e3 * (t1 - t0):.1f} ms, dispatch {1e3 * (t2 - t1):.1f} ms, "
-                      f"combine {1e3 * (t4 - t3):.1f} ms (single thread)"}
+            "sample": f"{tokens} tokens of the {wl.tokens}-token workload recipe "
+                      f"(capacity {int(sub.capacity[0])}/expert), host core {core}; median of {reps} "
+                      f"runs per step: route {1e3 * med[0]:.1f} ms, dispatch {1e3 * med[1]:.1f} ms, "
+                      f"combine {1e3 * med[2]:.1f} ms (single thread, "
+                      f"{sum(t_r) + sum(t_d) + sum(t_c):.1f} s timed in all)"}
 
 
 def run(args):
@@ -246,11 +272,14 @@ def run(args):
     print(json.dumps(res), flush=True)
 
 
-def decode_latency(n=200):
+def decode_latency(reps=50, per_graph=20):
     """Latency of one die's decode batch (96 tokens, hidden 7168, 256 experts,
-    top-8): the two-step path (route, dispatch, combine) against the
-    single-launch route+dispatch, and combine capped at 16 workgroups.  Each
-    call is bracketed by its own events; means over n calls."""
+    top-8).  Each figure is the mean device time per call when `per_graph`
+    calls run back to back from one captured HIP graph, replayed `reps`
+    times: no host launch cost and no per-call event overhead, as in a
+    serving loop.  The two-step path (route, dispatch, combine) and the
+    route+dispatch entry are timed alone and as whole steps; the replayed
+    step's outputs are checked bit for bit against an eager run."""
     import numpy as np
     import torch
 
@@ -265,34 +294,55 @@ def decode_latency(n=200):
     lg = torch.from_numpy(logits).cuda()
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
     rargs = (b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"], b["dropped"])
-    plan.route(lg, *rargs, b["workspace"])
-    plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+    route = lambda: plan.route(lg, *rargs, b["workspace"])
+    dispatch = lambda: plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+    fused = lambda: plan.route_dispatch(lg, xd, *rargs, b["dispatch_buf"], b["workspace"])
+    combine = lambda: plan.combine(b["combine_buf"], M.FMT_BF16, b["slots"], b["topk_w"], y)
+    route()
+    dispatch()
     plan.expert_stub(b["counts"], b["dispatch_buf"], b["combine_buf"], b["workspace"])
+    combine()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in (("y", y), ("slots", b["slots"]), ("w", b["topk_w"]))}
     calls = {
-        "route": lambda: plan.route(lg, *rargs, b["workspace"]),
-        "dispatch": lambda: plan.dispatch(xd, b["slots"], b["dispatch_buf"]),
-        "route_dispatch_fused": lambda: plan.route_dispatch(lg, xd, *rargs, b["dispatch_buf"],
-                                                            b["workspace"]),
-        "combine": lambda: plan.combine(b["combine_buf"], M.FMT_BF16, b["slots"], b["topk_w"], y),
+        "route": route,
+        "dispatch": dispatch,
+        "route_dispatch_fused": fused,
+        "combine": combine,
         "combine_16wg": lambda: plan.combine_limited(b["combine_buf"], M.FMT_BF16, b["slots"],
                                                      b["topk_w"], y, 16),
+        "two_step": lambda: (route(), dispatch(), combine()),
+        "fused_step": lambda: (fused(), combine()),
+        "launch_floor": lambda: y[:1, :8].fill_(1),  # one tiny torch kernel
     }
-    calls["launch_floor"] = lambda: y[:1, :8].zero_()  # one tiny torch kernel
     res = {}
     for name, f in calls.items():
-        for _ in range(10):
-            f()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                f()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        for e0, e1 in ev:
-            e0.record()
-            f()
-            e1.record()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                f()
+        g.replay()
         torch.cuda.synchronize()
-        res[name + "_us"] = statistics.fmean(1e3 * e0.elapsed_time(e1) for e0, e1 in ev)
-    res["two_step_us"] = res["route_us"] + res["dispatch_us"] + res["combine_us"]
-    res["fused_us"] = res["route_dispatch_fused_us"] + res["combine_us"]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = 1e3 * e0.elapsed_time(e1) / (reps * per_graph)
+        if name in ("two_step", "fused_step"):
+            ok = all(bool(torch.equal(ref[k], v)) for k, v in
+                     (("y", y), ("slots", b["slots"]), ("w", b["topk_w"])))
+            res[name + "_replay_matches_eager"] = ok
+        del g
+    res["timing"] = f"HIP graph of {per_graph} back-to-back calls, {reps} replays"
     res["workload"] = f"decode: {wl.description}"
     return res
 
@@ -425,7 +475,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-expert", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-tokens", type=int, default=30720)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=4 << 30)
     ap.add_argument("--summarize-rocprof", metavar="DIR")

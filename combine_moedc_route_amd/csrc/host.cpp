@@ -284,8 +284,10 @@ moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, in
   const moedc_status st =
       check_route(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
   if (st != MOEDC_OK) return st;
-  const hipError_t e = moedc::launch_route(
-      route_args(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws), stream);
+  const moedc::RouteArgs ra =
+      route_args(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
+  const hipError_t e = (T > 0 && T <= moedc::kFusedMaxTokens) ? moedc::launch_route_small(ra, stream)
+                                                               : moedc::launch_route(ra, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }
 

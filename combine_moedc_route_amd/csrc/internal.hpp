@@ -18,7 +18,7 @@ constexpr int kMaxExperts = 1024;    // logical and physical
 constexpr int kMaxK = 16;            // entries per token
 constexpr int kMaxReplicas = 8;
 constexpr int kRouteTokens = 64;     // tokens per route block (4 lanes per token)
-constexpr int kFusedMaxTokens = 256; // largest batch of the single-launch route + dispatch
+constexpr int kFusedMaxTokens = 256; // largest batch of the small-batch route (+ dispatch) path
 constexpr int64_t kSlotAlign = 512;  // dispatch slot stride granularity
 constexpr int64_t kWsAlign = 256;
 // Expert GEMM work list: bands of kBandTiles channel tiles x all row tiles
@@ -103,6 +103,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
+// Batches of 1..kFusedMaxTokens tokens: wave-per-token top-k + one-block ranks.
+hipError_t launch_route_small(const RouteArgs &a, hipStream_t s);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_stub(const StubArgs &a, hipStream_t s);

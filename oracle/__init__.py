@@ -191,13 +191,17 @@ def expert_w8a8(cfg: Cfg, counts, dbuf, slot_stride, W, w_scale, ebuf=None):
     return ebuf
 
 
-def combine(cfg: Cfg, eout, fmt, slots, topk_w):
-    """eout: [S][H] uint16 (FMT_BF16) or [S][slot_stride] uint8 (FMT_Q8)."""
+def combine(cfg: Cfg, eout, fmt, slots, topk_w, out=None):
+    """eout: [S][H] uint16 (FMT_BF16) or [S][slot_stride] uint8 (FMT_Q8);
+    the result goes to ``out`` ([T][H] uint16) when given."""
     eout = np.ascontiguousarray(eout)
     slots = np.ascontiguousarray(slots, dtype=np.int32)
     w = np.ascontiguousarray(topk_w, dtype=np.float32)
     T = slots.shape[0]
-    y = np.empty((T, cfg.hidden), np.uint16)
+    if out is None:
+        out = np.empty((T, cfg.hidden), np.uint16)
+    assert out.shape == (T, cfg.hidden) and out.dtype == np.uint16 and out.flags.c_contiguous
+    y = out
     stride = eout.strides[0]
     _check(lib().orc_combine(C.byref(cfg.c), T, _p(eout), fmt, stride,
                              _p(slots), _p(w), _p(y)), "combine")

@@ -60,10 +60,11 @@ def test_route_empty_and_ragged_token_counts():
         compare_route(wl, gpu_route(plan, wl, logits)[0], oracle.route(cfg, logits))
 
 
+@pytest.mark.parametrize("T", [700, 200])   # large- and small-batch route kernels
 @pytest.mark.parametrize("score_fn", [W.SCORE_SOFTMAX, W.SCORE_SIGMOID_NORM])
-def test_route_ties_signed_zeros_and_degenerate_rows(score_fn):
+def test_route_ties_signed_zeros_and_degenerate_rows(score_fn, T):
     rng = np.random.default_rng(77)
-    T, E, K = 700, 64, 8
+    E, K = 64, 8
     menu = np.array([-1.0, -0.0, 0.0, 0.25, 1.0, 2.0], np.float32)
     logits = menu[rng.integers(0, len(menu), (T, E))]
     logits[:50] = 0.0                          # all-equal rows -> ids 0..K-1
@@ -83,6 +84,31 @@ def test_route_ties_signed_zeros_and_degenerate_rows(score_fn):
     got = gpu_route(M.Plan.from_workload(wl1), wl1, lg)[0]
     compare_route(wl1, got, want)
     assert got["dropped"] == 30
+
+
+@pytest.mark.parametrize("T", [1, 77, 256, 300])
+def test_route_widest_config(T):
+    """1024 experts (16 logits per lane in the small-batch kernel), 15 routed
+    picks + a shared expert, 3-copy replicas of the first 10 experts."""
+    E, K, R = 1000, 15, 3
+    rep = np.full((E, R), -1, np.int32)
+    rep[:, 0] = np.arange(E)
+    extra = E
+    for e in range(10):
+        rep[e, 1:] = [extra, extra + 1]
+        extra += 2
+    P = extra + 1                                   # + shared expert
+    assert P <= 1024
+    cap = np.full(P, max(4, T // 40), np.int32)     # some experts overflow
+    cap[-1] = T
+    wl = W.Workload("wide", "", T, 128, E, P, K, 1, W.SCORE_SIGMOID_NORM, cap, rep, 0, "normal")
+    plan = M.Plan.from_workload(wl)
+    logits = np.random.default_rng(5).standard_normal((T, E)).astype(np.float32)
+    logits[0, :] = 0.5                              # an all-equal row
+    want = oracle.route(oracle.Cfg.from_workload(wl), logits)
+    got = gpu_route(plan, wl, logits)[0]
+    compare_route(wl, got, want)
+    assert (want["topk_ids"][0, :K] == [rep[e, 0] for e in range(K)]).all()
 
 
 def test_route_deterministic():
