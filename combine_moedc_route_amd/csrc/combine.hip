@@ -7,10 +7,13 @@
 // acc = +0; acc = fma(w_j, y_j, acc) over the token's entries in route
 // order, dropped entries skipped; BF16 round-to-nearest-even at the end.
 //
-// Mapping: one wave64 per token (a grid-stride loop when the caller caps
-// the number of workgroups).  The token's H values are covered in
-// groups of kChunks 512-value chunks (lane l holds values 512c + 8l .. +8
-// of chunk c).  Within a group the wave walks the K expert rows in route
+// Mapping: a wave per work unit, a grid-stride loop when the caller caps
+// the number of workgroups.  A unit is a whole token on large batches, or
+// one 512-value chunk of a token on small ones (below kSplitTokens tokens),
+// so a decode batch of ~100 tokens still spreads over every CU; under a
+// workgroup cap the workgroups grow to 16 waves.  A unit's
+// values are covered in groups of CH 512-value chunks (lane l holds values
+// 512c + 8l .. +8 of chunk c).  Within a group the wave walks the K expert rows in route
 // order and, for each row, issues the loads of all kChunks chunks back to
 // back: a contiguous 7 KiB (BF16) run of one row instead of 1 KiB pieces of
 // K rows in turn, which keeps HBM row-buffer locality on a gather whose rows
@@ -28,6 +31,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kChunks = 7;  // 512-value chunks per group: 7168 = 2 groups
+constexpr int kSplitTokens = 2048;  // below this, one unit per 512-value chunk
 
 __device__ __forceinline__ uint4 load_nt16(const uint8_t *p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -45,8 +49,11 @@ __device__ __forceinline__ void store_nt16(uint16_t *p, const float (&acc)[8]) {
   __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(p));
 }
 
-template <int K, bool Q8>
-__device__ __forceinline__ void combine_token(const CombineArgs &a, int64_t t, int lane) {
+// Chunks [c0, c1) of token t, CH chunks at a time.  Each output value sees
+// the same K fmas in the same order whatever the unit shape.
+template <int K, bool Q8, int CH>
+__device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, int c0, int c1,
+                                             int lane) {
   const int H = a.H;
   int slot[K];
   float w[K];
@@ -56,26 +63,26 @@ __device__ __forceinline__ void combine_token(const CombineArgs &a, int64_t t, i
     w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
   }
   uint16_t *yrow = a.y + t * H;
-  const int nch = (H + 511) / 512;
-  for (int g0 = 0; g0 < nch; g0 += kChunks) {
-    float acc[kChunks][8];
+  const int hend = min(H, 512 * c1);  // values of this unit end here
+  for (int g0 = c0; g0 < c1; g0 += CH) {
+    float acc[CH][8];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint8_t *row = a.eout + (int64_t)(slot[k] < 0 ? 0 : slot[k]) * a.eout_stride;
       if (!Q8) {
-        uint4 v[kChunks];
+        uint4 v[CH];
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
+        for (int c = 0; c < CH; ++c) {
           const int e = (g0 + c) * 512 + lane * 8;
           v[c] = make_uint4(0, 0, 0, 0);
-          if (slot[k] >= 0 && e < H) v[c] = load_nt16(row + (int64_t)e * 2);
+          if (slot[k] >= 0 && e < hend) v[c] = load_nt16(row + (int64_t)e * 2);
         }
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
+        for (int c = 0; c < CH; ++c) {
           const uint32_t d[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -84,20 +91,20 @@ __device__ __forceinline__ void combine_token(const CombineArgs &a, int64_t t, i
           }
         }
       } else {
-        uint2 v[kChunks];
-        float sc[kChunks];
+        uint2 v[CH];
+        float sc[CH];
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
+        for (int c = 0; c < CH; ++c) {
           const int e = (g0 + c) * 512 + lane * 8;
           v[c] = make_uint2(0, 0);
           sc[c] = 0.0f;
-          if (slot[k] >= 0 && e < H) {
+          if (slot[k] >= 0 && e < hend) {
             v[c] = load_nt8(row + e);
             sc[c] = *reinterpret_cast<const float *>(row + H + (a.per_token ? 0 : 4 * (e >> 7)));
           }
         }
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
+        for (int c = 0; c < CH; ++c) {
           const uint32_t d[2] = {v[c].x, v[c].y};
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -108,20 +115,31 @@ __device__ __forceinline__ void combine_token(const CombineArgs &a, int64_t t, i
       }
     }
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const int e = (g0 + c) * 512 + lane * 8;
-      if (e < H) store_nt16(yrow + e, acc[c]);
+      if (e < hend) store_nt16(yrow + e, acc[c]);
     }
   }
 }
 
-template <int K, bool Q8>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+// SPLIT: units are single 512-value chunks; otherwise whole tokens.  WPB
+// waves per workgroup (16 when the caller caps the workgroup count, so the
+// few CUs it gets still hold many loads in flight).
+template <int K, bool Q8, bool SPLIT, int WPB>
+__global__ __launch_bounds__(64 * WPB) void combine_kernel(CombineArgs a) {
   const int lane = lane_id();
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6); t < a.T;
-       t += stride) {
-    combine_token<K, Q8>(a, t, lane);
+  const int nch = (a.H + 511) / 512;
+  const int64_t units = SPLIT ? (int64_t)a.T * nch : a.T;
+  const int64_t stride = (int64_t)gridDim.x * WPB;
+  for (int64_t u = (int64_t)blockIdx.x * WPB + uniform(threadIdx.x >> 6); u < units;
+       u += stride) {
+    if (SPLIT) {
+      const int64_t t = u / nch;
+      const int c = (int)(u - t * nch);
+      combine_unit<K, Q8, 1>(a, t, c, c + 1, lane);
+    } else {
+      combine_unit<K, Q8, kChunks>(a, u, 0, nch, lane);
+    }
   }
 }
 
@@ -129,21 +147,36 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int64_t need = (a.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  // Small batches: chunk units, with 16-wave workgroups when the caller's
+  // cap leaves fewer 4-wave workgroups than chunk units need.
+  const bool split = a.T < kSplitTokens;
+  const int64_t units = split ? a.T * (int64_t)((a.H + 511) / 512) : a.T;
+  const bool wide = split && (int64_t)a.max_blocks * kWavesPerBlock < units;
+  const int wpb = wide ? 16 : kWavesPerBlock;
+  const int64_t need = (units + wpb - 1) / wpb;
   const unsigned grid = (unsigned)(need < a.max_blocks ? need : a.max_blocks);
   const bool q8 = a.fmt == MOEDC_FMT_Q8;
   switch (a.K) {
-#define MOEDC_CASE(k)                                                  \
-  case k:                                                              \
-    if (q8)                                                            \
-      combine_kernel<k, true><<<grid, 256, 0, s>>>(a);                 \
-    else                                                               \
-      combine_kernel<k, false><<<grid, 256, 0, s>>>(a);                \
+#define MOEDC_LAUNCH(k, q)                                                     \
+  if (!split)                                                                  \
+    combine_kernel<k, q, false, kWavesPerBlock><<<grid, 256, 0, s>>>(a);       \
+  else if (!wide)                                                              \
+    combine_kernel<k, q, true, kWavesPerBlock><<<grid, 256, 0, s>>>(a);        \
+  else                                                                         \
+    combine_kernel<k, q, true, 16><<<grid, 1024, 0, s>>>(a);
+#define MOEDC_CASE(k)          \
+  case k:                      \
+    if (q8) {                  \
+      MOEDC_LAUNCH(k, true)    \
+    } else {                   \
+      MOEDC_LAUNCH(k, false)   \
+    }                          \
     break;
     MOEDC_CASE(1) MOEDC_CASE(2) MOEDC_CASE(3) MOEDC_CASE(4) MOEDC_CASE(5) MOEDC_CASE(6)
     MOEDC_CASE(7) MOEDC_CASE(8) MOEDC_CASE(9) MOEDC_CASE(10) MOEDC_CASE(11) MOEDC_CASE(12)
     MOEDC_CASE(13) MOEDC_CASE(14) MOEDC_CASE(15) MOEDC_CASE(16)
 #undef MOEDC_CASE
+#undef MOEDC_LAUNCH
     default:
       return hipErrorInvalidValue;
   }

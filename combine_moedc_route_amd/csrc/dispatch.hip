@@ -20,6 +20,10 @@
 // K slots, with the non-temporal hint (slots are written once and read by
 // a later kernel).  Many waves per CU overlap one token's loads with other
 // tokens' quantize and store phases.
+//
+// Small batches (below kSplitTokens tokens, 128-value groups) use one wave
+// per 512-value chunk of a token instead, so ~100 decode tokens still keep
+// every CU busy; the bytes written are the same.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -31,6 +35,7 @@ namespace moedc {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kSplitTokens = 2048;
 
 template <int NCH, bool PER_TOKEN>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
@@ -90,10 +95,44 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   }
 }
 
+// One wave per (token, 512-value chunk); 128-value groups only.
+__global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
+  const int lane = lane_id();
+  const int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
+  const int64_t t = u / nch;
+  if (t >= a.T) return;
+  const int c = (int)(u - t * nch);
+  const int H = a.H;
+  const int e = c * 512 + lane * 8;
+  // The token's slots (lane k holds entry k) load alongside the values.
+  const int my_slot = lane < a.K ? a.slots[t * a.K + lane] : -1;
+  const uint4 v = e < H ? reinterpret_cast<const uint4 *>(a.x + t * H)[c * 64 + lane]
+                        : make_uint4(0, 0, 0, 0);
+  const uint32_t m = row16_max_u32(absmax8(v));
+  const float sc = __uint_as_float(m << 16) / 127.0f;
+  const uint2 q = quant8(v, sc);
+  for (int k = 0; k < a.K; ++k) {
+    const int slot = __builtin_amdgcn_readlane(my_slot, k);
+    if (slot < 0) continue;
+    uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
+    if (e < H) {
+      const u32x2 qq = {q.x, q.y};
+      __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
+      if ((lane & 15) == 0) __builtin_nontemporal_store(sc, reinterpret_cast<float *>(dst + H + 4 * (e >> 7)));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.T < kSplitTokens && !a.per_token) {
+    const int nch = (a.H + 511) / 512;
+    const int64_t units = (int64_t)a.T * nch;
+    dispatch_split<<<(unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock), 256, 0, s>>>(a, nch);
+    return hipGetLastError();
+  }
   const int nch = (a.H + 511) / 512;
   const unsigned grid = (unsigned)((a.T + kWavesPerBlock - 1) / kWavesPerBlock);
   switch (nch) {

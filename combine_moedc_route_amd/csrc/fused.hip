@@ -62,114 +62,115 @@ __device__ __forceinline__ float wave_sum(float z) {
   return z;
 }
 
+// Float back from a key (the -0 of a tie pair comes back as +0, which no
+// gate can tell apart).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // ---- 1. top-k, gates and physical ids: one wave per token -------------------
-template <int KR, bool SHARED>
+// NV = logits per lane (a power of two >= E / 64).  A key of 0 marks an
+// empty or already picked entry: every finite logit's key is above it.
+template <int NV, bool SHARED>
 __global__ __launch_bounds__(256) void topk_wave(RouteArgs a) {
-  constexpr int KT = KR + (SHARED ? 1 : 0);
+  __shared__ float pick_v[4][kMaxK];
+  __shared__ int pick_e[4][kMaxK];
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+  const int wv = uniform(threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + wv;
   if (t >= a.T) return;
-  const int E = a.E, P = a.P;
+  const int E = a.E, P = a.P, KR = a.KR;
   const float *row = a.logits + (int64_t)t * E;
 
-  float v[kVals];
-  uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not yet picked
+  float v[NV];
+  uint32_t key[NV];
 #pragma unroll
-  for (int i = 0; i < kVals; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    v[i] = 0.0f;
-    if (64 * i < E && e < E) {
-      v[i] = row[e];
-      live |= 1u << i;
-    }
+    v[i] = e < E ? row[e] : 0.0f;
+    key[i] = e < E ? fkey(v[i]) : 0u;
   }
 
-  float pv[KR];
-  int pid[KR];
-#pragma unroll
   for (int j = 0; j < KR; ++j) {
-    // Best live entry of this lane: ids ascend with i, so the first of equal
-    // keys is the lower id.
-    uint32_t bk = 0;
-    int bi = 0x7FFFFFFF;
+    // Best entry of this lane: ids ascend with i, so the first of equal keys
+    // is the lower id.
+    uint32_t bk = key[0];
+    int bi = lane;
 #pragma unroll
-    for (int i = 0; i < kVals; ++i) {
-      const uint32_t k = fkey(v[i]);
-      if (((live >> i) & 1u) && (bi == 0x7FFFFFFF || k > bk)) {
-        bk = k;
+    for (int i = 1; i < NV; ++i)
+      if (key[i] > bk) {
+        bk = key[i];
         bi = lane + 64 * i;
       }
-    }
-    const uint32_t m = wave_max_u32(bi == 0x7FFFFFFF ? 0u : bk);
-    const uint64_t cand = __ballot(bi != 0x7FFFFFFF && bk == m);
+    const uint32_t m = wave_max_u32(bk);
+    const uint64_t cand = __ballot(bk == m);
     int id;
-    if (__popcll(cand) == 1) {
+    if (__popcll(cand) == 1)
       id = __builtin_amdgcn_readlane(bi, (int)__ffsll((long long)cand) - 1);
-    } else {  // equal keys in several lanes: the lowest id wins
-      id = (int)wave_min_u32((cand >> lane) & 1u ? (uint32_t)bi : 0xFFFFFFFFu);
-    }
-    // Only non-finite rows can leave nothing to pick; keep the id valid.
-    if (id >= E) id = 0;
-    pid[j] = id;
-    // The winning lane retires the entry and broadcasts its value.
-    float val = 0.0f;
+    else  // equal keys in several lanes: the lowest id wins
+      id = (int)wave_min_u32(bk == m ? (uint32_t)bi : 0xFFFFFFFFu);
+    if (m == 0u || id >= E) id = 0;  // nothing left: only non-finite rows
 #pragma unroll
-    for (int i = 0; i < kVals; ++i)
-      if (lane + 64 * i == id) {
-        val = v[i];
-        live &= ~(1u << i);
-      }
-    pv[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val), id & 63));
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i == id) key[i] = 0u;
+    if (lane == 0) {
+      pick_v[wv][j] = key_float(m);
+      pick_e[wv][j] = id;
+    }
   }
+  // Lane 0's LDS writes above precede the reads below in this wave's
+  // in-order LDS queue.
+  __builtin_amdgcn_wave_barrier();
 
-  // ---- gates (every lane holds the same picks) ----
-  float w[KT];
+  // ---- gates: lane j finishes pick j (sums in pick order, as the
+  // large-batch kernel does) ----
+  float wj = 0.0f;
   if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
-    const float mx = pv[0];
+    const float mx = pick_v[wv][0];
     float z = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kVals; ++i)
-      if ((lane + 64 * i) < E && 64 * i < E) z += expf(v[i] - mx);
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i < E) z += expf(v[i] - mx);
     const float Z = wave_sum(z);
-#pragma unroll
-    for (int j = 0; j < KR; ++j) w[j] = expf(pv[j] - mx) / Z;
+    if (lane < KR) wj = expf(pick_v[wv][lane] - mx) / Z;
   } else {
-    float sg[KR];
-    float S = 0.0f;
-#pragma unroll
+    float S = 0.0f, sj = 0.0f;
     for (int j = 0; j < KR; ++j) {
-      sg[j] = 1.0f / (1.0f + expf(-pv[j]));
-      S += sg[j];
+      const float sg = 1.0f / (1.0f + expf(-pick_v[wv][j]));
+      S += sg;
+      if (j == lane) sj = sg;
     }
-#pragma unroll
-    for (int j = 0; j < KR; ++j) w[j] = sg[j] / S;
+    wj = sj / S;
   }
-  int pk[KT];
-#pragma unroll
-  for (int j = 0; j < KR; ++j) pk[j] = a.rep_table[pid[j] * a.R + t % a.rep_count[pid[j]]];
-  if (SHARED) {
-    pk[KT - 1] = P - 1;
-    w[KT - 1] = 1.0f;
+  const int KT = KR + (SHARED ? 1 : 0);
+  if (lane < KR) {
+    const int e = pick_e[wv][lane];
+    a.topk_ids[(int64_t)t * KT + lane] = a.R == 1 ? e : a.rep_table[e * a.R + t % a.rep_count[e]];
+    a.topk_w[(int64_t)t * KT + lane] = wj;
+  } else if (SHARED && lane == KR) {
+    a.topk_ids[(int64_t)t * KT + lane] = P - 1;
+    a.topk_w[(int64_t)t * KT + lane] = 1.0f;
   }
-#pragma unroll
-  for (int j = 0; j < KT; ++j)
-    if (lane == j) {
-      a.topk_ids[(int64_t)t * KT + j] = pk[j];
-      a.topk_w[(int64_t)t * KT + j] = w[j];
-    }
 }
 
 // ---- shared pieces of the rank kernels ----------------------------------------
 struct RankLds {
   unsigned long long mask[kMaxExperts][kMaskWords];
+  int cap[kMaxExperts];
+  int capbase[kMaxExperts];
   int wave_sum[kBlock / 64];
   int wave_drop[kBlock / 64];
 };
 
-// mask[p] bit t: token t chose physical expert p (from the written ids).
+// mask[p] bit t: token t chose physical expert p (from the written ids);
+// the static capacities and bases are staged alongside (P <= kBlock).
 __device__ __forceinline__ void build_masks(const RouteArgs &a, RankLds &L) {
   const int tid = threadIdx.x;
   for (int i = tid; i < a.P * kMaskWords; i += kBlock) L.mask[i / kMaskWords][i % kMaskWords] = 0ull;
+  if (tid < a.P) {
+    L.cap[tid] = a.cap[tid];
+    L.capbase[tid] = a.capbase[tid];
+  }
   __syncthreads();
   const int n = a.T * a.K;
   for (int i = tid; i < n; i += kBlock) {
@@ -204,7 +205,7 @@ __device__ __forceinline__ void counts_offsets(const RouteArgs &a, RankLds &L) {
     if ((tid & 63) >= d) incl += u;
   }
   if ((tid & 63) == 63) L.wave_sum[tid >> 6] = incl;
-  const int drop = tid < P ? max(0, cnt - a.cap[tid]) : 0;
+  const int drop = tid < P ? max(0, cnt - L.cap[tid]) : 0;
   int dsum = drop;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) dsum += __shfl_xor(dsum, d);
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void rank_single(RouteArgs a) {
   for (int i = threadIdx.x; i < n; i += kBlock) {
     const int t = i / a.K, p = a.topk_ids[i];
     const int r = rank_of(L, p, t);
-    a.slots[i] = r < a.cap[p] ? a.capbase[p] + r : -1;
+    a.slots[i] = r < L.cap[p] ? L.capbase[p] + r : -1;
   }
 }
 
@@ -242,23 +243,24 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   __shared__ uint32_t chunk_max[kBlock / 64];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  build_masks(ra, L);
-  if (blockIdx.x == 0) counts_offsets(ra, L);
-  if (tid < ra.K) {
-    const int p = ra.topk_ids[(int64_t)t * ra.K + tid];
-    const int r = rank_of(L, p, t);
-    const int slot = r < ra.cap[p] ? ra.capbase[p] + r : -1;
-    slot_of[tid] = slot;
-    ra.slots[(int64_t)t * ra.K + tid] = slot;
-  }
-  __syncthreads();
-
-  // wave c quantizes values 512 c .. 512 c + 511 of the token
+  // wave c quantizes values 512 c .. 512 c + 511 of the token; its load is
+  // issued first so that it overlaps the rank work.
   const int wave = uniform(tid >> 6), lane = lane_id();
   const int H = da.H;
   const int e = wave * 512 + lane * 8;
   uint4 v = make_uint4(0, 0, 0, 0);
   if (e < H) v = reinterpret_cast<const uint4 *>(da.x + (int64_t)t * H)[wave * 64 + lane];
+
+  build_masks(ra, L);
+  if (blockIdx.x == 0) counts_offsets(ra, L);
+  if (tid < ra.K) {
+    const int p = ra.topk_ids[(int64_t)t * ra.K + tid];
+    const int r = rank_of(L, p, t);
+    const int slot = r < L.cap[p] ? L.capbase[p] + r : -1;
+    slot_of[tid] = slot;
+    ra.slots[(int64_t)t * ra.K + tid] = slot;
+  }
+  __syncthreads();
   uint32_t m = row16_max_u32(absmax8(v));
   if (PER_TOKEN) {
     m = max(m, (uint32_t)__shfl_xor((int)m, 16));
@@ -287,28 +289,23 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   }
 }
 
-template <int KR>
-hipError_t launch_topk_kr(const RouteArgs &a, hipStream_t s) {
+template <int NV>
+hipError_t launch_topk_nv(const RouteArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.T + 3) / 4);
   if (a.shared)
-    topk_wave<KR, true><<<grid, 256, 0, s>>>(a);
+    topk_wave<NV, true><<<grid, 256, 0, s>>>(a);
   else
-    topk_wave<KR, false><<<grid, 256, 0, s>>>(a);
+    topk_wave<NV, false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_small(const RouteArgs &a, hipStream_t s) {
-  switch (a.KR) {
-#define MOEDC_CASE(k) \
-  case k:             \
-    return launch_topk_kr<k>(a, s);
-    MOEDC_CASE(1) MOEDC_CASE(2) MOEDC_CASE(3) MOEDC_CASE(4) MOEDC_CASE(5) MOEDC_CASE(6)
-    MOEDC_CASE(7) MOEDC_CASE(8) MOEDC_CASE(9) MOEDC_CASE(10) MOEDC_CASE(11) MOEDC_CASE(12)
-    MOEDC_CASE(13) MOEDC_CASE(14) MOEDC_CASE(15) MOEDC_CASE(16)
-#undef MOEDC_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
+  if (a.KR < 1 || a.KR > kMaxK || a.E > kMaxExperts) return hipErrorInvalidValue;
+  if (a.E <= 64) return launch_topk_nv<1>(a, s);
+  if (a.E <= 128) return launch_topk_nv<2>(a, s);
+  if (a.E <= 256) return launch_topk_nv<4>(a, s);
+  if (a.E <= 512) return launch_topk_nv<8>(a, s);
+  return launch_topk_nv<16>(a, s);
 }
 
 }  // namespace

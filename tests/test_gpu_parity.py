@@ -2,6 +2,8 @@
 same seeded inputs.  Integer, index and byte outputs must match bit for bit;
 gates within the derived fp32 tolerance; combine output within 1 BF16 ulp
 (and is expected to be bit-identical: same operations, same order)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -185,6 +187,30 @@ def test_combine_parity(name, fmt):
     got = host_u16(y)
     assert ulp_diff_bf16(got, want).max(initial=0) <= 1
     assert np.array_equal(got, want), f"{(got != want).sum()} elements differ by 1 ulp"
+
+
+@pytest.mark.parametrize("T", [2047, 2048, 2051])
+def test_dispatch_combine_around_split_threshold(T):
+    """Token counts on both sides of the small-batch mapping (one wave per
+    512-value chunk below 2048 tokens), ragged last workgroups, partial last
+    chunk (H = 1152), capacity overflow."""
+    cap = np.full(40, 400, np.int32)
+    cap[0] = 200                                # one expert overflows
+    wl = dataclasses.replace(W.get("ragged"), tokens=T, capacity=cap)
+    log(f"[case] ragged T={T}")
+    x, logits = W.make_inputs(wl)
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    r = oracle.route(cfg, logits)
+    dbuf = gpu_dispatch(plan, x, r["slots"])
+    check_dispatch_tokens(dbuf, x, r["slots"], np.arange(T), wl.hidden)
+    check_dispatch_untouched(dbuf, r["slots"], wl.hidden)
+    _, ebuf = _combine_inputs(wl, x, cfg, plan, r)
+    want = oracle.combine(cfg, ebuf, M.FMT_BF16, r["slots"], r["topk_w"])
+    y = torch.full((T, wl.hidden), -1, dtype=torch.int16, device="cuda")
+    plan.combine(dev_i16(ebuf), M.FMT_BF16, dev(r["slots"]), dev(r["topk_w"]), y)
+    assert np.array_equal(host_u16(y), want)
+    log(f"  dropped {r['dropped']}; dispatch and combine bit-exact")
 
 
 def test_combine_dropped_entries_and_signed_zero():
