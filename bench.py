@@ -450,8 +450,10 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
                      f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
                      f"{copy_bytes}-byte copy); valid while source_sha matches."}
-    for key, tag in (("combine", "combine_kernel<8, false>"), ("dispatch", "dispatch_kernel<14, false>"),
-                     ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm(")):
+    # Kernels of the global workload's launches (whole-token combine, BF16).
+    for key, tag in (("combine", "combine_kernel<8, false, false, 4>"),
+                     ("dispatch", "dispatch_kernel<14, false>"),
+                     ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm<true>(")):
         kf = [k for k in fetch if tag in k]
         kw = [k for k in write if tag in k]
         if not kf or not kw:

@@ -183,14 +183,14 @@ moedc_status moedc_combine(const moedc_plan *plan, int32_t num_tokens,
 /*
  * Routing and dispatch in one call, for small decode batches.  Same outputs
  * and the same dispatch buffer bytes as moedc_route followed by
- * moedc_dispatch (softmax gates may differ in the last bits: the softmax
- * denominator is summed in a different order; sigmoid-normalised gates are
- * identical).  For 1 <= num_tokens <= 256 it is a single kernel launch in
- * which every workgroup recomputes the routing of the whole batch and then
- * quantizes and stores one token ("Decode Phase": 96 tokens per die;
- * "FusedDispatch and FusedCombine": routing metadata fused with the token
- * exchange); larger batches run the two-step path.  Arguments, layouts,
- * alignment and errors are those of moedc_route and moedc_dispatch.
+ * moedc_dispatch, bit for bit.  For 1 <= num_tokens <= 256 it is two
+ * launches with no host step between them: a wave-per-token top-k, then
+ * one workgroup per token that derives its slots from every token's picks
+ * and immediately quantizes and stores that token ("Decode Phase": 96
+ * tokens per die; "FusedDispatch and FusedCombine": routing metadata fused
+ * with the token exchange); larger batches run the two-step path.
+ * Arguments, layouts, alignment and errors are those of moedc_route and
+ * moedc_dispatch.
  */
 moedc_status moedc_route_dispatch(const moedc_plan *plan, int32_t num_tokens,
                                   const float *logits, const uint16_t *x,
@@ -199,8 +199,8 @@ moedc_status moedc_route_dispatch(const moedc_plan *plan, int32_t num_tokens,
                                   void *dispatch_buf, void *workspace, hipStream_t stream);
 
 /*
- * moedc_combine on at most max_workgroups workgroups (each runs 4 token
- * waves and loops over the batch), leaving the other compute units to
+ * moedc_combine on at most max_workgroups workgroups (each loops over the
+ * batch; below 2048 tokens they run 16 waves each), leaving the other compute units to
  * concurrent work on other streams -- the pages' decode pipeline gives the
  * MoE path a fixed share of the cores ("Micro-batch Decode Pipeline" of the
  * CloudMatrix384 article).  Output identical to moedc_combine.
