@@ -123,10 +123,17 @@ def cpu_baseline(tokens=30720, reps=3):
     finally:
         os.sched_setaffinity(0, old)
     med = [statistics.median(v) for v in (t_r, t_d, t_c)]
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     sec = sum(med)
     return {"value": tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{tokens} tokens of the {wl.tokens}-token workload recipe "
-                      f"(capacity {int(sub.capacity[0])}/expert), host core {core}; median of {reps} "
+                      f"(capacity {int(sub.capacity[0])}/expert), 1 core ({model}, core {core}); "
+                      f"median of {reps} "
                       f"runs per step: route {1e3 * med[0]:.1f} ms, dispatch {1e3 * med[1]:.1f} ms, "
                       f"combine {1e3 * med[2]:.1f} ms (single thread, "
                       f"{sum(t_r) + sum(t_d) + sum(t_c):.1f} s timed in all)"}
@@ -245,12 +252,16 @@ def run(args):
         "combine_us": mean(c_us),
         "dispatch_us_median": statistics.median(d_us),
         "combine_us_median": statistics.median(c_us),
+        "dispatch_us_min": min(d_us),
+        "combine_us_min": min(c_us),
         "dispatch_plus_combine_us": dc_us,
         "dispatch_plus_combine_tokens_per_s": T / (dc_us * 1e-6),
         "dispatch_GBps": disp_gbps,
         "combine_GBps": comb_gbps,
         "dispatch_plus_combine_GBps": dc_gbps,
         "dispatch_plus_combine_frac_of_hbm_peak": dc_gbps / HBM_PEAK_GBPS,
+        "dispatch_frac_of_hbm_peak": disp_gbps / HBM_PEAK_GBPS,
+        "combine_frac_of_hbm_peak": comb_gbps / HBM_PEAK_GBPS,
         "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": cb, "route": ab["route"]},
         "roofline": {
             "kernel": dom,
