@@ -192,9 +192,28 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
     stage(Xs[0], Ws[0], sx, fetch_step(a, wtile, slot0, rows, chans, 0, spg, tid), 0, spg, tid);
     StepRegs nxt = fetch_step(a, wtile, slot0, rows, chans, min(1, ksteps - 1), spg, tid);
 
+    // Waves 4-7 (the second wave on each SIMD) fold a step's group sums
+    // after the next barrier, while waves 0-3 run that step's MFMAs, and run
+    // their own MFMAs while waves 0-3 fold: the matrix and vector units of a
+    // SIMD stay busy together instead of taking turns.
+    const bool lag = G128 && wave >= 4;
     for (int g = 0; g < ksteps; ++g) {
       const int buf = g & 1;
+      float sv[4];
+      if (lag && g > 0) {
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) sv[tf] = sx[(g - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
+      }
       __syncthreads();  // step g staged by all; step g-1's reads of buf^1 done
+      if (lag && g > 0) {
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf)
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              accf[nf][tf][q] = __builtin_fmaf(sv[tf], (float)acc[nf][tf][q], accf[nf][tf][q]);
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         v4i av[4], bv[4];
@@ -216,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
       if (g + 1 < ksteps) stage(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
       if (g + 2 < ksteps) nxt = fetch_step(a, wtile, slot0, rows, chans, g + 2, spg, tid);
 
-      if (g % spg == spg - 1) {  // end of an activation-scale group
+      if (!lag && g % spg == spg - 1) {  // end of an activation-scale group
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf) {
           const float s = sx[(g / spg) & 1][64 * wm + 16 * tf + (lane & 15)];
@@ -228,6 +247,17 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
             if (!G128) acc[nf][tf] = v4i{0, 0, 0, 0};
           }
         }
+      }
+    }
+    if (lag) {  // the last step's fold (its scales are not restaged before the next tile)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) {
+        const float s = sx[(ksteps - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            accf[nf][tf][q] = __builtin_fmaf(s, (float)acc[nf][tf][q], accf[nf][tf][q]);
       }
     }
 
