@@ -110,8 +110,10 @@ template <int KR, bool SHARED>
 __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   constexpr int KT = KR + (SHARED ? 1 : 0);
   __shared__ float tile[kRouteTokens][kTileE + 1];
-  __shared__ float lval[kRouteTokens][kSub][KR];
-  __shared__ int lid[kRouteTokens][kSub][KR];
+  // Token-minor, so the merge's reads (lane = token, each at its own list
+  // position) hit distinct banks.
+  __shared__ float lval[kSub][KR][kRouteTokens];
+  __shared__ int lid[kSub][KR][kRouteTokens];
   __shared__ float zpart[kRouteTokens][kSub];
   __shared__ float mrow[kRouteTokens];
   __shared__ unsigned long long tokmask[kMaxExperts];
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < KR; ++j) {
-    lval[r][sub][j] = val[j];
-    lid[r][sub][j] = id[j];
+    lval[sub][j][r] = val[j];
+    lid[sub][j][r] = id[j];
   }
   __syncthreads();
 
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < kSub; ++s2) {
         if (h[s2] < KR) {
-          const float v = lval[tid][s2][h[s2]];
-          const int i = lid[tid][s2][h[s2]];
+          const float v = lval[s2][h[s2]][tid];
+          const int i = lid[s2][h[s2]][tid];
           if (bs < 0 || v > bv || (v == bv && i < bi)) {
             bv = v;
             bi = i;
