@@ -274,6 +274,23 @@ def run(args):
         },
         "wall_s_timed": wall,
     }
+    if fmt == M.FMT_BF16:
+        # The same combine reading the INT8 dispatch slots (identity experts /
+        # quantized return), timed over the two dispatch buffer sets.
+        cq = []
+        for i in range(args.warmup + args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            plan.combine(sets[i & 1][0], M.FMT_Q8, slots, w, y)
+            e1.record()
+            if i >= args.warmup:
+                cq.append((e0, e1))
+        torch.cuda.synchronize()
+        q_us = [1e3 * e0.elapsed_time(e1) for e0, e1 in cq]
+        q_gbps = ab["combine_q8"] / (mean(q_us) * 1e-6) / 1e9
+        res["combine_q8"] = {"us": mean(q_us), "us_median": statistics.median(q_us),
+                             "GBps": q_gbps, "frac_of_hbm_peak": q_gbps / HBM_PEAK_GBPS,
+                             "algorithmic_bytes": ab["combine_q8"]}
     if args.workload == "global" and not args.no_expert:
         res["expert_gemm"] = expert_gemm(plan, wl, counts, sets[0][0], sets[0][1], ws, xd, slots)
     if args.workload == "global" and not args.no_decode:
