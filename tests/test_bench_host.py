@@ -1,0 +1,86 @@
+"""bench.py host logic (no GPU): the algorithmic byte counts behind every
+roofline figure, the rocprofv3 counter bookkeeping, and the one-GPU guard."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_match_the_workload_table():
+    # Global workload (30720 x 7168, top-8 of 256): dispatch reads x and the
+    # slots and writes K payload+scale rows; combine reads K BF16 rows, the
+    # slots and gates, and writes y.  Counted by hand from the layouts.
+    T, H, K, E, G = 30720, 7168, 8, 256, 56
+    ab = bench.algorithmic_bytes(T, H, K, E)
+    assert ab["dispatch"] == 2 * T * H + 4 * T * K + T * K * (H + 4 * G) == 2_258_042_880
+    assert ab["combine"] == 2 * T * K * H + 8 * T * K + 2 * T * H == 3_965_583_360
+    assert ab["combine_q8"] == T * K * (H + 4 * G) + 8 * T * K + 2 * T * H == 2_259_025_920
+    assert ab["route"] == 4 * T * E + 12 * T * K == 34_406_400
+    one = bench.algorithmic_bytes(1, H, K, E)
+    assert (one["dispatch"], one["combine"], one["combine_q8"]) == (73_504, 129_088, 73_536)
+    # Prefill with a shared expert (K = 9): 5,301,862,400 / 9,399,959,552 B.
+    pf = bench.algorithmic_bytes(65536, H, 9, E)
+    assert pf["dispatch"] == 5_301_862_400 and pf["combine"] == 9_399_959_552
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_summarize_rocprof_reads_stats_and_counters(tmp_path, capsys):
+    _write_csv(str(tmp_path / "p" / "x_kernel_stats.csv"),
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+               [["combine_kernel<8, false, false, 4>", 10, 732500, 720000, 750000, 55.5]])
+    _write_csv(str(tmp_path / "p" / "x_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [["k", "FETCH_SIZE", 10.0], ["k", "FETCH_SIZE", 30.0]])
+    out = tmp_path / "s.txt"
+    bench.summarize_rocprof(str(tmp_path / "p"), str(out))
+    text = out.read_text()
+    assert "732.50" in text and "720.00" in text and "750.00" in text
+    assert "    2                 20.0     FETCH_SIZE  k" in text
+
+
+def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    tf = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, false, 4>(moedc::CombineArgs)"
+    _write_csv(str(tmp_path / "f" / "f_counter_collection.csv"), hdr,
+               [[name, "FETCH_SIZE", 1000.0], [name, "FETCH_SIZE", 1000.0]])
+    _write_csv(str(tmp_path / "w" / "w_counter_collection.csv"), hdr, [[name, "WRITE_SIZE", 500.0]])
+    # A 4096-byte copy whose counters read 2 KiB fetched and 4 KiB written.
+    _write_csv(str(tmp_path / "cf" / "c_counter_collection.csv"), hdr,
+               [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 2.0]])
+    _write_csv(str(tmp_path / "cw" / "c_counter_collection.csv"), hdr,
+               [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 4.0]])
+    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+                         str(tmp_path / "cw"), 4096)
+    d = json.loads(tf.read_text())
+    assert d["combine"]["fetch_bytes"] == 1000 * 1024 * 2.0
+    assert d["combine"]["write_bytes"] == 500 * 1024 * 1.0
+    assert d["combine"]["source_sha"] == bench.source_sha(bench.KERNEL_SOURCES["combine"])
+    assert "dispatch" not in d
+    # The recorded figure is served while the kernel source is unchanged...
+    assert bench.measured_traffic("combine") == 1000 * 1024 * 2.0 + 500 * 1024
+    # ...and withheld once it changes.
+    d["combine"]["source_sha"] = "0" * 16
+    tf.write_text(json.dumps(d))
+    assert bench.measured_traffic("combine") is None
