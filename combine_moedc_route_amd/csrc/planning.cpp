@@ -10,6 +10,7 @@
 // "CloudMatrix384 ...", section "Decode Phase": redundant copies of experts
 // balance load.  Here units are any expert-major work items (an expert's
 // token block, a GEMM tile row) and workers are workgroups or devices.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <numeric>
