@@ -295,6 +295,8 @@ def run(args):
         res["expert_gemm"] = expert_gemm(plan, wl, counts, sets[0][0], sets[0][1], ws, xd, slots)
     if args.workload == "global" and not args.no_decode:
         res["decode_latency"] = decode_latency()
+    if args.workload == "global" and not args.no_placement:
+        res["placement"] = placement()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(res), flush=True)
@@ -421,6 +423,57 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, xd, slots, iters=5):
             "per_token_scales": {"us": us_pt, "TOPs": tops_pt, "frac": tops_pt / INT8_PEAK_TOPS}}
 
 
+def placement(workers=8, redundant=32, max_replicas=8):
+    """Load balancing on the skewed workload (Zipf(1.1) popularity over 256
+    experts, top-8, 30720 tokens): per-expert loads from the device route,
+    a redundant-copy table from moedc_place_replicas, the device route again
+    with the workload's fixed table and with the planned one (largest token
+    count per physical copy), and the expert layer's 128 x 256 tiles per
+    copy assigned to `workers` devices by moedc_lpt_partition vs round-robin."""
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+    wl = W.get("skewed")
+    T, E, KR, H = wl.tokens, wl.num_logical, wl.top_k, wl.hidden
+    _, logits = W.make_inputs(wl)
+    lg = torch.from_numpy(logits).cuda()
+
+    def route_counts(P, table):
+        plan = M.Plan(max_tokens=T, hidden=128, num_logical=E, num_phys=P, top_k=KR,
+                      capacity=np.full(P, T, np.int32), replica_table=table)
+        i32 = dict(dtype=torch.int32, device="cuda")
+        ws = torch.empty(plan.sizes.workspace_bytes, dtype=torch.uint8, device="cuda")
+        plan.bind_workspace(ws)
+        counts = torch.empty(P, **i32)
+        plan.route(lg, torch.empty((T, KR), **i32), torch.empty((T, KR), device="cuda"), counts,
+                   torch.empty(P + 1, **i32), torch.empty((T, KR), **i32), torch.empty(1, **i32), ws)
+        return counts.cpu().numpy().astype(np.int64)
+
+    load = route_counts(E, None)
+    t0 = time.perf_counter()
+    table = M.place_replicas(load.astype(np.float64), redundant, max_replicas)
+    t_place = time.perf_counter() - t0
+    fixed = route_counts(E + redundant, wl.replica_table)
+    planned = route_counts(E + redundant, table)
+    tiles = np.ceil(planned / 128.0) * (H // 256)
+    t0 = time.perf_counter()
+    assign, makespan = M.lpt_partition(tiles, workers)
+    t_lpt = time.perf_counter() - t0
+    rr = np.bincount(np.arange(tiles.size) % workers, weights=tiles, minlength=workers).max()
+    return {"workload": f"skewed: {wl.description}",
+            "max_tokens_per_copy": {"no_replicas": int(load.max()), "fixed_table": int(fixed.max()),
+                                    "planned_table": int(planned.max()),
+                                    "mean_per_copy": T * KR / (E + redundant)},
+            "experts_replicated": int(((table >= 0).sum(axis=1) > 1).sum()),
+            "max_copies": int((table >= 0).sum(axis=1).max()),
+            "place_replicas_us": 1e6 * t_place,
+            f"expert_tiles_on_{workers}_devices": {"lower_bound": float(tiles.sum() / workers),
+                                                  "round_robin": float(rr), "lpt": float(makespan)},
+            "lpt_partition_us": 1e6 * t_lpt}
+
+
 def calib_copy(args):
     """A plain device-to-device copy of a known byte count (reads N, writes N)."""
     import torch
@@ -520,6 +573,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-expert", action="store_true")
+    ap.add_argument("--no-placement", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=30720)
     ap.add_argument("--calib-copy", action="store_true")
