@@ -268,6 +268,38 @@ def test_combine_parity_full_size(name):
     log(f"  {len(toks)} sampled tokens bit-exact")
 
 
+@pytest.mark.parametrize("name", FULL)
+def test_combine_q8_full_size_sampled(name):
+    """Q8 combine over the GPU's own full-size dispatch; the oracle side
+    quantizes the sampled tokens itself into a compact slot buffer."""
+    wl, x, logits, plan, cfg = setup(name)
+    r = oracle.route(cfg, logits)
+    s = plan.sizes
+    T, H, K = x.shape[0], wl.hidden, wl.K
+    G = H // wl.group_size
+    dbuf = gpu_dispatch(plan, x, r["slots"])
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    plan.combine(dbuf, M.FMT_Q8, dev(r["slots"]), dev(r["topk_w"]), y)
+    toks = sample_tokens(T, 512, 8)
+    got = host_u16(y[torch.from_numpy(toks).cuda()])
+    del dbuf
+    q, sc = oracle.quantize_tokens(x[toks], wl.group_size)
+    rows = r["slots"][toks]
+    compact = np.zeros((int((rows >= 0).sum()), s.slot_stride), np.uint8)
+    remap = np.full(rows.shape, -1, np.int32)
+    idx = 0
+    for i in range(rows.shape[0]):
+        for k in range(K):
+            if rows[i, k] >= 0:
+                compact[idx, :H] = q[i].view(np.uint8)
+                compact[idx, H:H + 4 * G] = sc[i].view(np.uint8)
+                remap[i, k] = idx
+                idx += 1
+    want = oracle.combine(cfg, compact, M.FMT_Q8, remap, r["topk_w"][toks])
+    assert np.array_equal(got, want)
+    log(f"  {len(toks)} sampled tokens bit-exact (Q8)")
+
+
 # ------------------------------------------------------------------ expert stand-in
 
 @pytest.mark.parametrize("name", ["decode", "decode_pt", "ragged", "replica_shared", "overflow"])
