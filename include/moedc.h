@@ -87,7 +87,7 @@ typedef struct moedc_config {
 } moedc_config;
 
 typedef struct moedc_sizes {
-  int64_t workspace_bytes;      /* device workspace for route/stub (bind once) */
+  int64_t workspace_bytes;      /* device workspace for route, the expert layer and stand-in (bind once) */
   int64_t dispatch_buf_bytes;   /* total_slots * slot_stride */
   int64_t combine_buf_bytes;    /* total_slots * combine_slot_stride */
   int64_t slot_stride;          /* dispatch slot: round_up(H + 4*G, 512) bytes */
@@ -112,8 +112,10 @@ moedc_status moedc_plan_sizes(const moedc_plan *plan, moedc_sizes *out);
 
 /* Uploads the plan's static tables (capacities, slot bases, replica table)
  * into the caller's device workspace of workspace_bytes (16-byte aligned),
- * asynchronously on `stream`.  Needed once per workspace before route or
- * the expert stand-in use it. */
+ * asynchronously on `stream`.  Needed once per workspace before route,
+ * route_dispatch, the expert layer or the expert stand-in use it.  Calls
+ * that share a workspace must not overlap (route and the expert layer keep
+ * per-call work lists in it). */
 moedc_status moedc_plan_bind_workspace(const moedc_plan *plan, void *workspace,
                                        hipStream_t stream);
 
