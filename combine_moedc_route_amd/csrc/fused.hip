@@ -14,12 +14,13 @@
 //  2. rank_dispatch: one block per token.  Every block rebuilds per-expert
 //     token bit masks from the T x K ids in LDS (a few KB from L2), so the
 //     rank of token t at expert p -- the number of lower tokens that chose
-//     p -- is a popcount; its slots follow from the static bases.  Block 0
-//     also writes counts, offsets and the drop total.  The block then
-//     quantizes its token and stores it into its slots.
+//     p -- is a popcount; its slots follow from the static bases.  The
+//     block then quantizes its token and stores it into its slots; one
+//     extra block writes counts, offsets and the drop total.
 //
 // moedc_route on a small batch runs step 1 and rank_single, the mask and
-// rank work of step 2 in one block for all tokens.  Picks, counts, offsets,
+// rank work of step 2 for all tokens in one block (a second one writes the
+// counts, offsets and drops).  Picks, counts, offsets,
 // slots and dispatched bytes equal those of the large-batch kernels bit for
 // bit; sigmoid gates too (same per-token arithmetic), while a softmax
 // denominator is summed in another order (within the stated gate tolerance).
@@ -222,11 +223,15 @@ __device__ __forceinline__ void counts_offsets(const RouteArgs &a, RankLds &L) {
   }
 }
 
-// ---- 2a. ranks and slots of every token in one block (moedc_route) ----------
+// ---- 2a. ranks and slots of every token (moedc_route): block 0 writes the
+// slots, block 1 counts, offsets and drops, side by side -------------------
 __global__ __launch_bounds__(kBlock) void rank_single(RouteArgs a) {
   __shared__ RankLds L;
   build_masks(a, L);
-  counts_offsets(a, L);
+  if (blockIdx.x == 1) {
+    counts_offsets(a, L);
+    return;
+  }
   const int n = a.T * a.K;
   for (int i = threadIdx.x; i < n; i += kBlock) {
     const int t = i / a.K, p = a.topk_ids[i];
@@ -243,6 +248,11 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   __shared__ uint32_t chunk_max[kBlock / 64];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
+  if (t == ra.T) {  // the extra last block: counts, offsets, drops only
+    build_masks(ra, L);
+    counts_offsets(ra, L);
+    return;
+  }
   // wave c quantizes values 512 c .. 512 c + 511 of the token; its load is
   // issued first so that it overlaps the rank work.
   const int wave = uniform(tid >> 6), lane = lane_id();
@@ -252,7 +262,6 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   if (e < H) v = reinterpret_cast<const uint4 *>(da.x + (int64_t)t * H)[wave * 64 + lane];
 
   build_masks(ra, L);
-  if (blockIdx.x == 0) counts_offsets(ra, L);
   if (tid < ra.K) {
     const int p = ra.topk_ids[(int64_t)t * ra.K + tid];
     const int r = rank_of(L, p, t);
@@ -314,7 +323,7 @@ hipError_t launch_route_small(const RouteArgs &ra, hipStream_t s) {
   if (ra.T <= 0 || ra.T > kFusedMaxTokens || ra.P > kBlock) return hipErrorInvalidValue;
   hipError_t e = launch_topk_small(ra, s);
   if (e != hipSuccess) return e;
-  rank_single<<<1, kBlock, 0, s>>>(ra);
+  rank_single<<<2, kBlock, 0, s>>>(ra);
   return hipGetLastError();
 }
 
@@ -324,10 +333,11 @@ hipError_t launch_route_dispatch_fused(const RouteArgs &ra, const DispatchArgs &
     return hipErrorInvalidValue;
   hipError_t e = launch_topk_small(ra, s);
   if (e != hipSuccess) return e;
+  // One block per token plus one for counts, offsets and drops.
   if (da.per_token)
-    rank_dispatch<true><<<ra.T, kBlock, 0, s>>>(ra, da);
+    rank_dispatch<true><<<ra.T + 1, kBlock, 0, s>>>(ra, da);
   else
-    rank_dispatch<false><<<ra.T, kBlock, 0, s>>>(ra, da);
+    rank_dispatch<false><<<ra.T + 1, kBlock, 0, s>>>(ra, da);
   return hipGetLastError();
 }
 
