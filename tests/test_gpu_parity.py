@@ -300,6 +300,31 @@ def test_combine_q8_full_size_sampled(name):
     log(f"  {len(toks)} sampled tokens bit-exact (Q8)")
 
 
+def test_expert_layers_on_an_empty_batch_write_nothing():
+    """All counts zero (the route of an empty batch): the expert layer's tile
+    list is empty and neither it nor the stand-in writes anything."""
+    wl, x, logits, plan, cfg = setup("tiny")
+    s = plan.sizes
+    ws = torch.empty(s.workspace_bytes, dtype=torch.uint8, device="cuda")
+    plan.bind_workspace(ws)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    counts, offsets = torch.full((wl.num_phys,), -7, **i32), torch.full((wl.num_phys + 1,), -7, **i32)
+    dropped = torch.full((1,), -7, **i32)
+    empty = torch.empty((0, wl.K), **i32)
+    plan.route(torch.empty((0, wl.num_logical), dtype=torch.float32, device="cuda"), empty,
+               torch.empty((0, wl.K), dtype=torch.float32, device="cuda"), counts, offsets,
+               empty, dropped, ws, num_tokens=0)
+    torch.cuda.synchronize()
+    assert (counts.cpu().numpy() == 0).all() and int(dropped.item()) == 0
+    dbuf = torch.zeros(s.dispatch_buf_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((s.total_slots, wl.hidden), 0x7FC1, dtype=torch.int16, device="cuda")
+    Wt, wsc = W.make_expert_weights(3, wl.num_phys, wl.hidden)
+    plan.expert_w8a8(counts, dbuf, torch.from_numpy(Wt).cuda(), dev(wsc), out, ws)
+    plan.expert_stub(counts, dbuf, out, ws)
+    torch.cuda.synchronize()
+    assert bool((out == 0x7FC1).all())
+
+
 # ------------------------------------------------------------------ expert stand-in
 
 @pytest.mark.parametrize("name", ["decode", "decode_pt", "ragged", "replica_shared", "overflow"])
