@@ -36,17 +36,23 @@ static_assert(kRouteTokens * kSub == 256, "one token per lane of wave 0");
 
 // Insert (v, e) into a list kept in descending value order; equal values
 // keep the earlier (lower-id) entry first because ids arrive ascending.
+// Branch-free (selects only): slot j takes the new entry, or slot j-1's old
+// one when the new entry lands above it; slots are updated from the bottom
+// up, so slot j-1 is still unmodified when slot j reads it.
 template <int KR>
 __device__ __forceinline__ void topk_insert(float (&val)[KR], int (&id)[KR], float v, int e) {
 #pragma unroll
-  for (int j = KR - 1; j >= 0; --j) {
-    const int jp = j > 0 ? j - 1 : 0;
-    const bool shift = j > 0 && v > val[jp];  // the new value lands above slot j
-    if (v > val[j]) {
-      val[j] = shift ? val[jp] : v;
-      id[j] = shift ? id[jp] : e;
-    }
+  for (int j = KR - 1; j > 0; --j) {
+    const bool take = v > val[j];
+    const bool shift = v > val[j - 1];  // the new value lands above slot j
+    const float nv = shift ? val[j - 1] : v;
+    const int ni = shift ? id[j - 1] : e;
+    val[j] = take ? nv : val[j];
+    id[j] = take ? ni : id[j];
   }
+  const bool take0 = v > val[0];
+  val[0] = take0 ? v : val[0];
+  id[0] = take0 ? e : id[0];
 }
 
 // A thread's share of one 64-expert tile of the block's logits, held in
@@ -142,8 +148,14 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
     tile_store(tile, tr, vec4);
     __syncthreads();
     if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
-    const int c1 = min(16 * sub + 16, ec);
-    for (int c = 16 * sub; c < c1; ++c) topk_insert<KR>(val, id, tile[r][c], e0 + c);
+    if (ec == kTileE) {  // full tile (block-uniform): a fixed, unrolled scan
+#pragma unroll
+      for (int i = 0; i < kTileE / kSub; ++i)
+        topk_insert<KR>(val, id, tile[r][16 * sub + i], e0 + 16 * sub + i);
+    } else {
+      const int c1 = min(16 * sub + 16, ec);
+      for (int c = 16 * sub; c < c1; ++c) topk_insert<KR>(val, id, tile[r][c], e0 + c);
+    }
   }
 #pragma unroll
   for (int j = 0; j < KR; ++j) {
@@ -194,8 +206,13 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
       tile_store(tile, tr, vec4);
       __syncthreads();
       if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
-      const int c1 = min(16 * sub + 16, ec);
-      for (int c = 16 * sub; c < c1; ++c) z += expf(tile[r][c] - m);
+      if (ec == kTileE) {
+#pragma unroll
+        for (int i = 0; i < kTileE / kSub; ++i) z += expf(tile[r][16 * sub + i] - m);
+      } else {
+        const int c1 = min(16 * sub + 16, ec);
+        for (int c = 16 * sub; c < c1; ++c) z += expf(tile[r][c] - m);
+      }
     }
     zpart[r][sub] = z;
     __syncthreads();
