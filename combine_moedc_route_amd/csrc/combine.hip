@@ -19,7 +19,8 @@
 // K rows in turn, which keeps HBM row-buffer locality on a gather whose rows
 // are scattered over the slot buffer.  Expert rows and the output are
 // touched once, so loads and stores carry the non-temporal hint.  A dropped
-// entry loads nothing and contributes fma(0, 0, acc) = acc exactly.
+// entry (slot -1), like any slot outside the plan's buffer, loads nothing
+// and contributes fma(0, 0, acc) = acc exactly.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -55,11 +56,12 @@ template <int K, bool Q8, int CH>
 __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, int c0, int c1,
                                              int lane) {
   const int H = a.H;
-  int slot[K];
+  int slot[K];  // -1 for an entry that is skipped
   float w[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    slot[k] = uniform(a.slots[t * K + k]);
+    const int s = uniform(a.slots[t * K + k]);
+    slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
     w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
   }
   uint16_t *yrow = a.y + t * H;

@@ -18,7 +18,8 @@
 // writes the token's payload (8 bytes per lane, 512 contiguous bytes per
 // store instruction) and its scales (one dword per lane) into each of the
 // K slots, with the non-temporal hint (slots are written once and read by
-// a later kernel).  Many waves per CU overlap one token's loads with other
+// a later kernel).  Entries with slot -1 (dropped), or any slot outside the
+// plan's buffer, are skipped.  Many waves per CU overlap one token's loads with other
 // tokens' quantize and store phases.
 //
 // Small batches (below kSplitTokens tokens, 128-value groups) use one wave
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   const int32_t *srow = a.slots + t * a.K;
   for (int k = 0; k < a.K; ++k) {
     const int slot = uniform(srow[k]);
-    if (slot < 0) continue;
+    if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
     uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
   const uint2 q = quant8(v, sc);
   for (int k = 0; k < a.K; ++k) {
     const int slot = __builtin_amdgcn_readlane(my_slot, k);
-    if (slot < 0) continue;
+    if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
     uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
     if (e < H) {
       const u32x2 qq = {q.x, q.y};

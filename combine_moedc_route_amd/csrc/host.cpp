@@ -244,6 +244,7 @@ moedc::DispatchArgs dispatch_args(const moedc_plan *p, int32_t T, const uint16_t
   a.G = p->G;
   a.K = p->K;
   a.per_token = p->G == 1;
+  a.total_slots = (int32_t)p->total_slots;
   return a;
 }
 
@@ -264,6 +265,7 @@ moedc_status combine_impl(const moedc_plan *p, int32_t T, const void *eout, int3
   a.w = topk_w;
   a.y = y;
   a.eout_stride = fmt == MOEDC_FMT_Q8 ? p->slot_stride : p->combine_stride;
+  a.total_slots = (int32_t)p->total_slots;
   a.T = T;
   a.H = p->cfg.hidden;
   a.K = p->K;

@@ -60,7 +60,8 @@ struct DispatchArgs {
   uint8_t *dbuf;
   int64_t slot_stride;
   int32_t T, H, G, K;
-  int32_t per_token;  // one scale per token (G == 1) instead of per 128 values
+  int32_t per_token;    // one scale per token (G == 1) instead of per 128 values
+  int32_t total_slots;  // entries outside [0, total_slots) are skipped
 };
 
 struct CombineArgs {
@@ -69,6 +70,7 @@ struct CombineArgs {
   const float *w;
   uint16_t *y;
   int64_t eout_stride;  // bytes per slot row
+  int32_t total_slots;  // entries outside [0, total_slots) are skipped
   int32_t T, H, K, fmt;
   int32_t per_token;    // Q8 input: one scale per token
   int32_t max_blocks;   // grid cap (workgroups of 4 token waves); >= 1

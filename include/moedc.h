@@ -158,7 +158,8 @@ moedc_status moedc_route(const moedc_plan *plan, int32_t num_tokens,
  * [s*slot_stride, (s+1)*slot_stride) of dispatch_buf: INT8 payload at
  * [0, H), G fp32 scales (little-endian) at [H, H + 4*G); the rest of the
  * slot and slots no token maps to are not written.  Entries with slot -1
- * are skipped.
+ * (dropped) are skipped, and so is any slot outside [0, total_slots), so a
+ * corrupt slot table cannot make the kernel write outside dispatch_buf.
  * x: BF16 [num_tokens][H] (16-byte aligned); slots: from moedc_route;
  * dispatch_buf: dispatch_buf_bytes (16-byte aligned).  x must be finite.
  * Errors: INVALID_ARG, SHAPE, ALIGN, HIP.
@@ -170,8 +171,10 @@ moedc_status moedc_dispatch(const moedc_plan *plan, int32_t num_tokens,
 /*
  * Combine: for each token t and hidden index i,
  *   acc = +0.0f;  acc = fmaf(topk_w[t][j], y_j[i], acc)  for j = 0..k-1
- * skipping entries with slot -1, then y[t][i] = BF16 round-to-nearest-even
- * of acc.  y_j is the expert output in slot slots[t][j]:
+ * skipping entries with slot -1 (and any slot outside [0, total_slots),
+ * which is never read), then y[t][i] = BF16 round-to-nearest-even of acc.
+ * slots and topk_w are [num_tokens][k] as written by moedc_route.
+ * y_j is the expert output in slot slots[t][j]:
  *  fmt BF16: expert_out is [total_slots][H] BF16 (combine_buf_bytes);
  *  fmt Q8:   expert_out is a dispatch buffer, y_j[i] = (float)q * scale.
  * expert_out and y (BF16 [num_tokens][H]) are 16-byte aligned.

@@ -237,6 +237,49 @@ def test_combine_dropped_entries_and_signed_zero():
     assert (got[:3] == 0).all()
 
 
+@pytest.mark.parametrize("T", [300, 2500])     # chunk-unit and token-unit kernels
+def test_slots_outside_the_buffer_are_skipped(T):
+    """Entries outside [0, total_slots) are skipped like -1 by dispatch and
+    combine: buffers get a guard region past total_slots that stays untouched
+    and unread.  Expected values: the oracle with those entries set to -1."""
+    wl = W.Workload("guard", "", T, 640, 8, 8, 4, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(8, T, np.int32), None, 95, "normal")
+    log(f"[case] out-of-range slots T={T}")
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    s = plan.sizes
+    S, H, G, K = s.total_slots, wl.hidden, wl.hidden // 128, wl.K
+    x, logits = W.make_inputs(wl)
+    clean = oracle.route(cfg, logits)["slots"]
+    bad = clean.copy()
+    rng = np.random.default_rng(96)
+    pick = rng.random(bad.shape) < 0.25
+    menu = np.array([S, S + 1, S + 3, -2, -(2 ** 31)], np.int64)
+    bad[pick] = menu[rng.integers(0, len(menu), int(pick.sum()))].astype(np.int32)
+    clean[pick] = -1
+    guard = 4
+
+    dbuf = torch.full((S + guard, s.slot_stride), SENTINEL, dtype=torch.uint8, device="cuda")
+    plan.dispatch(dev_i16(x), dev(bad), dbuf)
+    torch.cuda.synchronize()
+    check_dispatch_tokens(dbuf, x, clean, np.arange(T), H)
+    check_dispatch_untouched(dbuf[:S], clean, H)
+    assert bool((dbuf[S:] == SENTINEL).all()), "dispatch wrote past total_slots"
+
+    dref = oracle.dispatch(cfg, x, clean, S, s.slot_stride)
+    ebuf = oracle.expert_stub(cfg, oracle.route(cfg, logits)["counts"], dref, s.slot_stride)
+    w = W.make_gates(97, T, K)
+    for fmt, src in ((M.FMT_BF16, ebuf), (M.FMT_Q8, dref)):
+        ref = oracle.combine(cfg, src, fmt, clean, w)
+        # guard rows that would change y if read: BF16 1.0, or q = 63 with scales ~0.75
+        junk = np.full((guard,) + src.shape[1:], 0x3F80 if src.dtype == np.uint16 else 0x3F,
+                       src.dtype)
+        full = np.concatenate([src, junk])
+        y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        plan.combine(dev_i16(full) if fmt == M.FMT_BF16 else dev(full), fmt, dev(bad), dev(w), y)
+        assert np.array_equal(host_u16(y), ref), f"fmt {fmt}"
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_combine_parity_full_size(name):
     wl, x, logits, plan, cfg = setup(name)
