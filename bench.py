@@ -295,6 +295,10 @@ def run(args):
         res["expert_gemm"] = expert_gemm(plan, wl, counts, sets[0][0], sets[0][1], ws, xd, slots)
     if args.workload == "global" and not args.no_decode:
         res["decode_latency"] = decode_latency()
+        # Batches of one token per wave or fewer take the one-launch route.
+        res["decode_latency"]["small_batches"] = {
+            str(n): decode_latency(tokens=n, which=("route", "route_dispatch_fused", "fused_step"))
+            for n in (1, 16)}
     if args.workload == "global" and not args.no_placement:
         res["placement"] = placement()
     if not args.no_cpu_baseline:
@@ -302,20 +306,26 @@ def run(args):
     print(json.dumps(res), flush=True)
 
 
-def decode_latency(reps=50, per_graph=20):
+def decode_latency(reps=50, per_graph=20, tokens=None, which=None):
     """Latency of one die's decode batch (96 tokens, hidden 7168, 256 experts,
     top-8).  Each figure is the mean device time per call when `per_graph`
     calls run back to back from one captured HIP graph, replayed `reps`
     times: no host launch cost and no per-call event overhead, as in a
     serving loop.  The two-step path (route, dispatch, combine) and the
     route+dispatch entry are timed alone and as whole steps; the replayed
-    step's outputs are checked bit for bit against an eager run."""
+    step's outputs are checked bit for bit against an eager run.  `tokens`
+    replaces the batch size (same capacities), `which` restricts the calls
+    timed."""
+    import dataclasses
+
     import numpy as np
     import torch
 
     from combine_moedc_route_amd import moedc as M
     from combine_moedc_route_amd import workloads as W
     wl = W.get("decode")
+    if tokens is not None:
+        wl = dataclasses.replace(wl, tokens=tokens)
     T, H, K = wl.tokens, wl.hidden, wl.K
     plan = M.Plan.from_workload(wl)
     b = plan.alloc("cuda:0")
@@ -347,6 +357,8 @@ def decode_latency(reps=50, per_graph=20):
     }
     res = {}
     for name, f in calls.items():
+        if which is not None and name not in which:
+            continue
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -373,7 +385,7 @@ def decode_latency(reps=50, per_graph=20):
             res[name + "_replay_matches_eager"] = ok
         del g
     res["timing"] = f"HIP graph of {per_graph} back-to-back calls, {reps} replays"
-    res["workload"] = f"decode: {wl.description}"
+    res["workload"] = f"decode: {wl.description}" if tokens is None else f"decode with {T} tokens"
     return res
 
 
@@ -598,7 +610,11 @@ def main():
         calib_copy(args)
         return
     if args.decode_only:
-        print(json.dumps(decode_latency()), flush=True)
+        res = decode_latency()
+        res["small_batches"] = {
+            str(n): decode_latency(tokens=n, which=("route", "route_dispatch_fused", "fused_step"))
+            for n in (1, 16)}
+        print(json.dumps(res), flush=True)
         return
     run(args)
 

@@ -188,12 +188,14 @@ moedc_status moedc_combine(const moedc_plan *plan, int32_t num_tokens,
 /*
  * Routing and dispatch in one call, for small decode batches.  Same outputs
  * and the same dispatch buffer bytes as moedc_route followed by
- * moedc_dispatch, bit for bit.  For 1 <= num_tokens <= 256 it is two
+ * moedc_dispatch, bit for bit.  For 17 <= num_tokens <= 256 it is two
  * launches with no host step between them: a wave-per-token top-k, then
  * one workgroup per token that derives its slots from every token's picks
  * and immediately quantizes and stores that token ("Decode Phase": 96
  * tokens per die; "FusedDispatch and FusedCombine": routing metadata fused
- * with the token exchange); larger batches run the two-step path.
+ * with the token exchange).  Up to 16 tokens it is one launch: every
+ * workgroup runs the batch's top-k itself.  Larger batches run the
+ * two-step path.
  * Arguments, layouts, alignment and errors are those of moedc_route and
  * moedc_dispatch.
  */
