@@ -58,11 +58,29 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
   const int H = a.H;
   int slot[K];  // -1 for an entry that is skipped
   float w[K];
+  if (CH == 1) {
+    // Chunk units (small batches, latency-bound): all 2K loads of the
+    // token's slots and gates are issued before any is used, one memory
+    // latency instead of K dependent ones.
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int s = uniform(a.slots[t * K + k]);
-    slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
-    w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
+    for (int k = 0; k < K; ++k) slot[k] = a.slots[t * K + k];
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = a.w[t * K + k];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = uniform(slot[k]);
+      slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
+      w[k] = slot[k] >= 0 ? w[k] : 0.0f;
+    }
+  } else {
+    // Whole tokens (large batches, many waves per CU hide the latency):
+    // gates of skipped entries are not read.
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int s = uniform(a.slots[t * K + k]);
+      slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
+      w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
+    }
   }
   uint16_t *yrow = a.y + t * H;
   const int hend = min(H, 512 * c1);  // values of this unit end here
@@ -135,9 +153,9 @@ __global__ __launch_bounds__(64 * WPB) void combine_kernel(CombineArgs a) {
   const int64_t stride = (int64_t)gridDim.x * WPB;
   for (int64_t u = (int64_t)blockIdx.x * WPB + uniform(threadIdx.x >> 6); u < units;
        u += stride) {
-    if (SPLIT) {
-      const int64_t t = u / nch;
-      const int c = (int)(u - t * nch);
+    if (SPLIT) {  // below kSplitTokens * 16 units: 32-bit division
+      const int t = (int)u / nch;
+      const int c = (int)u - t * nch;
       combine_unit<K, Q8, 1>(a, t, c, c + 1, lane);
     } else {
       combine_unit<K, Q8, kChunks>(a, u, 0, nch, lane);

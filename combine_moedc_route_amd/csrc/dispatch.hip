@@ -99,10 +99,11 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
 // One wave per (token, 512-value chunk); 128-value groups only.
 __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
   const int lane = lane_id();
-  const int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
-  const int64_t t = u / nch;
+  // Below kSplitTokens tokens of at most 16 chunks: 32-bit unit indices.
+  const int u = (int)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x >> 6);
+  const int t = u / nch;
   if (t >= a.T) return;
-  const int c = (int)(u - t * nch);
+  const int c = u - t * nch;
   const int H = a.H;
   const int e = c * 512 + lane * 8;
   // The token's slots (lane k holds entry k) load alongside the values.

@@ -92,11 +92,15 @@ __device__ __forceinline__ void topk_picks(const RouteArgs &a, int t, int lane, 
   const int E = a.E, KR = a.KR;
   const float *row = a.logits + (int64_t)t * E;
   uint32_t key[NV];
+  // Unconditional loads (lanes past E read entry E-1 and drop it) so that
+  // all NV loads are in flight together behind one wait.
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
     key[i] = e < E ? fkey(v[i]) : 0u;
+    v[i] = e < E ? v[i] : 0.0f;
   }
 
   for (int j = 0; j < KR; ++j) {
