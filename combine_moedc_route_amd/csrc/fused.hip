@@ -212,14 +212,25 @@ __device__ __forceinline__ void clear_masks(const RouteArgs &a, RankLds &L) {
   }
 }
 
-// Masks from the ids written by topk_wave.
-__device__ __forceinline__ void build_masks(const RouteArgs &a, RankLds &L) {
+// Masks from the ids written by topk_wave.  The ids (at most kIdsPerThread
+// per thread) are loaded before the masks are cleared, so their latency
+// overlaps that of the capacities instead of following it.
+// Entry i = threadIdx.x + r * kBlock of the batch goes to id[r].
+constexpr int kIdsPerThread = kFusedMaxTokens * kMaxK / kBlock;
+__device__ __forceinline__ void build_masks(const RouteArgs &a, RankLds &L,
+                                            int (&id)[kIdsPerThread]) {
+  const int n = a.T * a.K;  // >= 1
+#pragma unroll
+  for (int r = 0; r < kIdsPerThread; ++r) id[r] = a.topk_ids[min((int)threadIdx.x + r * kBlock, n - 1)];
   clear_masks(a, L);
   __syncthreads();
-  const int n = a.T * a.K;
-  for (int i = threadIdx.x; i < n; i += kBlock) {
-    const int t = i / a.K;
-    atomicOr(&L.mask[a.topk_ids[i]][t >> 6], 1ull << (t & 63));
+#pragma unroll
+  for (int r = 0; r < kIdsPerThread; ++r) {
+    const int i = threadIdx.x + r * kBlock;
+    if (i < n) {
+      const int t = i / a.K;
+      atomicOr(&L.mask[id[r]][t >> 6], 1ull << (t & 63));
+    }
   }
   __syncthreads();
 }
@@ -281,16 +292,21 @@ __device__ __forceinline__ void counts_offsets(const RouteArgs &a, RankLds &L) {
 // slots, block 1 counts, offsets and drops, side by side -------------------
 __global__ __launch_bounds__(kBlock) void rank_single(RouteArgs a) {
   __shared__ RankLds L;
-  build_masks(a, L);
+  int id[kIdsPerThread];
+  build_masks(a, L, id);
   if (blockIdx.x == 1) {
     counts_offsets(a, L);
     return;
   }
   const int n = a.T * a.K;
-  for (int i = threadIdx.x; i < n; i += kBlock) {
-    const int t = i / a.K, p = a.topk_ids[i];
-    const int r = rank_of(L, p, t);
-    a.slots[i] = r < L.cap[p] ? L.capbase[p] + r : -1;
+#pragma unroll
+  for (int r = 0; r < kIdsPerThread; ++r) {
+    const int i = threadIdx.x + r * kBlock;
+    if (i < n) {
+      const int t = i / a.K, p = id[r];
+      const int rk = rank_of(L, p, t);
+      a.slots[i] = rk < L.cap[p] ? L.capbase[p] + rk : -1;
+    }
   }
 }
 
@@ -338,8 +354,9 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   __shared__ uint32_t chunk_max[kBlock / 64];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
+  int id[kIdsPerThread];
   if (t == ra.T) {  // the extra last block: counts, offsets, drops only
-    build_masks(ra, L);
+    build_masks(ra, L, id);
     counts_offsets(ra, L);
     return;
   }
@@ -350,10 +367,11 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
   const int e = wave * 512 + lane * 8;
   uint4 v = make_uint4(0, 0, 0, 0);
   if (e < H) v = reinterpret_cast<const uint4 *>(da.x + (int64_t)t * H)[wave * 64 + lane];
+  const int own = ra.topk_ids[(int64_t)t * ra.K + min(tid, ra.K - 1)];  // entry tid, tid < K
 
-  build_masks(ra, L);
+  build_masks(ra, L, id);
   if (tid < ra.K) {
-    const int p = ra.topk_ids[(int64_t)t * ra.K + tid];
+    const int p = own;
     const int r = rank_of(L, p, t);
     const int slot = r < L.cap[p] ? L.capbase[p] + r : -1;
     slot_of[tid] = slot;
