@@ -81,14 +81,20 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // The pieces below are shared by every small-batch kernel, so all of them
 // pick, weight and map a token's experts with the same instructions.
 
-// K_R rounds of a wave-wide argmax over (value desc, id asc): pick j's value
-// and logical id go to pv[j], pe[j] (written by lane 0); v[] keeps the
-// token's logits.  NV = logits per lane (a power of two >= E / 64).  A key
-// of 0 marks an empty or already picked entry: every finite logit's key is
-// above it.
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// K_R rounds of a wave-wide argmax over (value desc, id asc); lane j < K_R
+// receives pick j's value (pv) and logical id (pe); v[] keeps the token's
+// logits.  NV = logits per lane (a power of two >= E / 64).  A key of 0
+// marks an empty or already picked entry: every finite logit's key is
+// above it.  The rounds are bound by the dependent cross-lane steps (DPP
+// row max, readlanes, ballot); sorting each lane's candidates once instead
+// of scanning them every round measured no faster.
 template <int NV>
 __device__ __forceinline__ void topk_picks(const RouteArgs &a, int t, int lane, float (&v)[NV],
-                                           float *pv, int *pe) {
+                                           float &pv, int &pe) {
   const int E = a.E, KR = a.KR;
   const float *row = a.logits + (int64_t)t * E;
   uint32_t key[NV];
@@ -103,9 +109,11 @@ __device__ __forceinline__ void topk_picks(const RouteArgs &a, int t, int lane, 
     v[i] = e < E ? v[i] : 0.0f;
   }
 
+  pv = 0.0f;
+  pe = 0;
   for (int j = 0; j < KR; ++j) {
-    // Best entry of this lane: ids ascend with i, so the first of equal keys
-    // is the lower id.
+    // This lane's best candidate (ids ascend with i, so the first of equal
+    // keys is the lower id).
     uint32_t bk = key[0];
     int bi = lane;
 #pragma unroll
@@ -125,66 +133,57 @@ __device__ __forceinline__ void topk_picks(const RouteArgs &a, int t, int lane, 
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       if (lane + 64 * i == id) key[i] = 0u;
-    if (lane == 0) {
-      pv[j] = key_float(m);
-      pe[j] = id;
+    if (lane == j) {
+      pv = key_float(m);
+      pe = id;
     }
   }
-  // Lane 0's LDS writes above precede later reads in this wave's in-order
-  // LDS queue.
-  __builtin_amdgcn_wave_barrier();
 }
 
 // Gate of pick `lane` (lanes < K_R; sums in pick order, as the large-batch
-// kernel does).
+// kernel does).  pv: this lane's pick value from topk_picks.
 template <int NV>
 __device__ __forceinline__ float topk_gate(const RouteArgs &a, int lane, const float (&v)[NV],
-                                           const float *pv) {
+                                           float pv) {
   const int E = a.E, KR = a.KR;
   float wj = 0.0f;
   if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
-    const float mx = pv[0];
+    const float mx = readlane_f(pv, 0);
     float z = 0.0f;
 #pragma unroll
     for (int i = 0; i < NV; ++i)
       if (lane + 64 * i < E) z += expf(v[i] - mx);
     const float Z = wave_sum(z);
-    if (lane < KR) wj = expf(pv[lane] - mx) / Z;
+    if (lane < KR) wj = expf(pv - mx) / Z;
   } else {
-    float S = 0.0f, sj = 0.0f;
-    for (int j = 0; j < KR; ++j) {
-      const float sg = 1.0f / (1.0f + expf(-pv[j]));
-      S += sg;
-      if (j == lane) sj = sg;
-    }
-    wj = sj / S;
+    // Lane j evaluates pick j's sigmoid; the sum still runs in pick order.
+    const float sg = 1.0f / (1.0f + expf(-pv));
+    float S = 0.0f;
+    for (int j = 0; j < KR; ++j) S += readlane_f(sg, j);
+    wj = sg / S;
   }
   return wj;
 }
 
-// Physical id of entry `lane` of token t: pick `lane` mapped to its replica
-// copy t mod r_e, the shared expert after the routed picks, -1 past K.
+// Physical id of entry `lane` of token t: pick `lane` (pe) mapped to its
+// replica copy t mod r_e, the shared expert after the routed picks, -1
+// past K.
 template <bool SHARED>
-__device__ __forceinline__ int entry_id(const RouteArgs &a, int t, int lane, const int *pe) {
-  if (lane < a.KR) {
-    const int e = pe[lane];
-    return a.R == 1 ? e : a.rep_table[e * a.R + t % a.rep_count[e]];
-  }
+__device__ __forceinline__ int entry_id(const RouteArgs &a, int t, int lane, int pe) {
+  if (lane < a.KR) return a.R == 1 ? pe : a.rep_table[pe * a.R + t % a.rep_count[pe]];
   return SHARED && lane == a.KR ? a.P - 1 : -1;
 }
 
 template <int NV, bool SHARED>
 __global__ __launch_bounds__(256) void topk_wave(RouteArgs a) {
-  __shared__ float pick_v[4][kMaxK];
-  __shared__ int pick_e[4][kMaxK];
   const int lane = lane_id();
-  const int wv = uniform(threadIdx.x >> 6);
-  const int t = blockIdx.x * 4 + wv;
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (t >= a.T) return;
-  float v[NV];
-  topk_picks<NV>(a, t, lane, v, pick_v[wv], pick_e[wv]);
-  const float wj = topk_gate<NV>(a, lane, v, pick_v[wv]);
-  const int id = entry_id<SHARED>(a, t, lane, pick_e[wv]);
+  float v[NV], pv;
+  int pe;
+  topk_picks<NV>(a, t, lane, v, pv, pe);
+  const float wj = topk_gate<NV>(a, lane, v, pv);
+  const int id = entry_id<SHARED>(a, t, lane, pe);
   if (lane < a.K) {
     a.topk_ids[(int64_t)t * a.K + lane] = id;
     a.topk_w[(int64_t)t * a.K + lane] = lane < a.KR ? wj : 1.0f;
@@ -391,31 +390,27 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
 // Physical ids of every token into ids[t][*]; gates and route outputs of
 // token `own`, or of every token when own < 0.
 template <int NV, bool SHARED>
-__device__ __forceinline__ void topk_all(const RouteArgs &a, int own, int (*ids)[kMaxK],
-                                         float (*pv)[kMaxK], int (*pe)[kMaxK]) {
+__device__ __forceinline__ void topk_all(const RouteArgs &a, int own, int (*ids)[kMaxK]) {
   const int wave = uniform(threadIdx.x >> 6), lane = lane_id();
   for (int t = wave; t < a.T; t += kBlock / 64) {
-    float v[NV];
-    topk_picks<NV>(a, t, lane, v, pv[wave], pe[wave]);
-    const int id = entry_id<SHARED>(a, t, lane, pe[wave]);
+    float v[NV], pv;
+    int pe;
+    topk_picks<NV>(a, t, lane, v, pv, pe);
+    const int id = entry_id<SHARED>(a, t, lane, pe);
     if (lane < a.K) ids[t][lane] = id;
     if (own < 0 || t == own) {
-      const float wj = topk_gate<NV>(a, lane, v, pv[wave]);
+      const float wj = topk_gate<NV>(a, lane, v, pv);
       if (lane < a.K) {
         a.topk_ids[(int64_t)t * a.K + lane] = id;
         a.topk_w[(int64_t)t * a.K + lane] = lane < a.KR ? wj : 1.0f;
       }
     }
-    // This token's reads of pv / pe come before the next token's writes.
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
 struct OneLds {
   RankLds L;
   int ids[kOneLaunchTokens][kMaxK];
-  float pick_v[kBlock / 64][kMaxK];
-  int pick_e[kBlock / 64][kMaxK];
   int slot_of[kMaxK];
   uint32_t chunk_max[kBlock / 64];
 };
@@ -426,7 +421,7 @@ template <int NV, bool SHARED>
 __global__ __launch_bounds__(kBlock) void route_one(RouteArgs a) {
   __shared__ OneLds S;
   clear_masks(a, S.L);
-  topk_all<NV, SHARED>(a, blockIdx.x == 0 ? -1 : a.T, S.ids, S.pick_v, S.pick_e);
+  topk_all<NV, SHARED>(a, blockIdx.x == 0 ? -1 : a.T, S.ids);
   __syncthreads();
   fill_masks(a, S.L, S.ids);
   if (blockIdx.x == 1) {
@@ -453,7 +448,7 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_one(RouteArgs ra, Dispa
   uint4 v = make_uint4(0, 0, 0, 0);  // the token's load overlaps the routing
   if (t < ra.T && e < H) v = reinterpret_cast<const uint4 *>(da.x + (int64_t)t * H)[wave * 64 + lane];
   clear_masks(ra, S.L);
-  topk_all<NV, SHARED>(ra, t, S.ids, S.pick_v, S.pick_e);
+  topk_all<NV, SHARED>(ra, t, S.ids);
   __syncthreads();
   fill_masks(ra, S.L, S.ids);
   if (t == ra.T) {
