@@ -170,7 +170,7 @@ __device__ __forceinline__ float topk_gate(const RouteArgs &a, int lane, const f
 // past K.
 template <bool SHARED>
 __device__ __forceinline__ int entry_id(const RouteArgs &a, int t, int lane, int pe) {
-  if (lane < a.KR) return a.R == 1 ? pe : a.rep_table[pe * a.R + t % a.rep_count[pe]];
+  if (lane < a.KR) return a.rep_identity ? pe : a.rep_table[pe * a.R + t % a.rep_count[pe]];
   return SHARED && lane == a.KR ? a.P - 1 : -1;
 }
 

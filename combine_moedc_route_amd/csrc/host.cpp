@@ -115,6 +115,9 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
       }
       p->rep_count[(size_t)e] = r;
     }
+    p->rep_identity = 1;
+    for (int32_t e = 0; e < E; ++e)
+      if (p->rep_count[(size_t)e] != 1 || p->rep_table[(size_t)e * R] != e) p->rep_identity = 0;
     p->cfg.capacity = p->cap.data();
     p->cfg.replica_table = c.replica_table ? p->rep_table.data() : nullptr;
     p->K = c.top_k + c.num_shared;
@@ -229,6 +232,7 @@ moedc::RouteArgs route_args(const moedc_plan *p, int32_t T, const float *logits,
   a.KR = p->cfg.top_k;
   a.shared = p->cfg.num_shared;
   a.score_fn = p->cfg.score_fn;
+  a.rep_identity = p->rep_identity;
   return a;
 }
 

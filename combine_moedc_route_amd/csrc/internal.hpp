@@ -52,6 +52,7 @@ struct RouteArgs {
   const int32_t *rep_table;
   int32_t *block_counts;
   int32_t T, E, P, R, K, KR, shared, score_fn;
+  int32_t rep_identity;  // every logical expert e is physical expert e (one copy)
 };
 
 struct DispatchArgs {
@@ -120,6 +121,7 @@ struct moedc_plan {
   moedc_config cfg;                 // pointer fields point into the vectors below
   std::vector<int32_t> cap, capbase, rep_count, rep_table;
   int32_t K, G, nblk_max;
+  int32_t rep_identity;             // no replicas and logical e == physical e
   int32_t gemm_nbe, gemm_J;         // expert GEMM bands per expert / per XCD
   int64_t slot_stride, combine_stride, total_slots;
   moedc::WsLayout ws;

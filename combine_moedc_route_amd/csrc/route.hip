@@ -238,9 +238,9 @@ __global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
       for (int j = 0; j < KR; ++j) w[j] = sg[j] / S;
     }
 #pragma unroll
-    for (int j = 0; j < KR; ++j) {
+    for (int j = 0; j < KR; ++j) {  // replica copy t mod r_e
       const int e = id[j];
-      pk[j] = a.rep_table[e * a.R + (int)t % a.rep_count[e]];
+      pk[j] = a.rep_identity ? e : a.rep_table[e * a.R + (int)t % a.rep_count[e]];
     }
     if (SHARED) {
       pk[KT - 1] = P - 1;

@@ -571,6 +571,35 @@ def test_expert_w8a8_full_size_sampled():
         assert np.array_equal(got, want), p
 
 
+@pytest.mark.parametrize("T", [5, 100, 700])   # one-launch, two-launch and large-batch routes
+def test_route_one_copy_table_that_is_not_the_identity(T):
+    """A one-column replica table may still place logical expert e on another
+    physical id; every route path must follow it."""
+    E, P = 32, 40
+    table = ((7 * np.arange(E) + 3) % P).astype(np.int32).reshape(E, 1)
+    assert len(set(table[:, 0])) == E and (table[:, 0] != np.arange(E)).any()
+    wl = W.Workload("perm", "", T, 256, E, P, 6, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(P, T, np.int32), table, 77, "normal")
+    log(f"[case] permuted one-copy table T={T}")
+    x, logits = W.make_inputs(wl)
+    plan = M.Plan.from_workload(wl)
+    want = oracle.route(oracle.Cfg.from_workload(wl), logits)
+    assert set(np.unique(want["topk_ids"])) <= set(table[:, 0])
+    got, ws = gpu_route(plan, wl, logits)
+    compare_route(wl, got, want)
+    dbuf = gpu_dispatch(plan, x, want["slots"])
+    fbuf = torch.full_like(dbuf, SENTINEL)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    o = [torch.empty((T, wl.K), **i32), torch.empty((T, wl.K), device="cuda"),
+         torch.empty(P, **i32), torch.empty(P + 1, **i32), torch.empty((T, wl.K), **i32),
+         torch.empty(1, **i32)]
+    plan.route_dispatch(dev(logits), dev_i16(x), *o, fbuf, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(o[0].cpu().numpy(), want["topk_ids"])
+    assert np.array_equal(o[4].cpu().numpy(), want["slots"])
+    assert torch.equal(fbuf, dbuf)
+
+
 def test_route_eight_copy_replicas():
     """Replica rows of up to 8 copies (the layout the load-proportional
     placement produces), on the skewed logits."""
