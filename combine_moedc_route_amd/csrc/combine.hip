@@ -33,6 +33,10 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kChunks = 7;  // 512-value chunks per group: 7168 = 2 groups
 constexpr int kSplitTokens = 2048;  // below this, one unit per 512-value chunk
+// Chunks per unit under a workgroup cap: 2 (twice the loads in flight per
+// wave), 1 from K = 14 on, where two chunks' loads no longer fit in the
+// 128 registers of a 16-wave workgroup.
+__host__ __device__ constexpr int wide_chunks(int k) { return k >= 14 ? 1 : 2; }
 
 __device__ __forceinline__ uint4 load_nt16(const uint8_t *p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -58,7 +62,7 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
   const int H = a.H;
   int slot[K];  // -1 for an entry that is skipped
   float w[K];
-  if (CH == 1) {
+  if (CH < kChunks) {
     // Chunk units (small batches, latency-bound): all 2K loads of the
     // token's slots and gates are issued before any is used, one memory
     // latency instead of K dependent ones.
@@ -142,23 +146,25 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
   }
 }
 
-// SPLIT: units are single 512-value chunks; otherwise whole tokens.  WPB
-// waves per workgroup (16 when the caller caps the workgroup count, so the
-// few CUs it gets still hold many loads in flight).
-template <int K, bool Q8, bool SPLIT, int WPB>
+// SPLIT: units are UC consecutive 512-value chunks of a token; otherwise
+// whole tokens.  WPB waves per workgroup (16 when the caller caps the
+// workgroup count, so the few CUs it gets still hold many loads in flight;
+// their units are then wide_chunks(K) chunks).
+template <int K, bool Q8, bool SPLIT, int WPB, int UC>
 __global__ __launch_bounds__(64 * WPB) void combine_kernel(CombineArgs a) {
   const int lane = lane_id();
   const int nch = (a.H + 511) / 512;
-  const int64_t units = SPLIT ? (int64_t)a.T * nch : a.T;
+  const int nu = (nch + UC - 1) / UC;  // units per token when SPLIT
+  const int64_t units = SPLIT ? (int64_t)a.T * nu : a.T;
   const int64_t stride = (int64_t)gridDim.x * WPB;
   for (int64_t u = (int64_t)blockIdx.x * WPB + uniform(threadIdx.x >> 6); u < units;
        u += stride) {
     if (SPLIT) {  // below kSplitTokens * 16 units: 32-bit division
-      const int t = (int)u / nch;
-      const int c = (int)u - t * nch;
-      combine_unit<K, Q8, 1>(a, t, c, c + 1, lane);
+      const int t = (int)u / nu;
+      const int c = ((int)u - t * nu) * UC;
+      combine_unit<K, Q8, UC>(a, t, c, min(c + UC, nch), lane);
     } else {
-      combine_unit<K, Q8, kChunks>(a, u, 0, nch, lane);
+      combine_unit<K, Q8, kChunks>(a, u, 0, nch, lane);  // two groups of kChunks
     }
   }
 }
@@ -170,20 +176,23 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   // Small batches: chunk units, with 16-wave workgroups when the caller's
   // cap leaves fewer 4-wave workgroups than chunk units need.
   const bool split = a.T < kSplitTokens;
-  const int64_t units = split ? a.T * (int64_t)((a.H + 511) / 512) : a.T;
+  const int nch = (a.H + 511) / 512;
+  const int64_t units = split ? a.T * (int64_t)nch : a.T;
   const bool wide = split && (int64_t)a.max_blocks * kWavesPerBlock < units;
   const int wpb = wide ? 16 : kWavesPerBlock;
-  const int64_t need = (units + wpb - 1) / wpb;
+  const int uc = wide_chunks(a.K);
+  const int64_t wunits = wide ? a.T * (int64_t)((nch + uc - 1) / uc) : units;
+  const int64_t need = (wunits + wpb - 1) / wpb;
   const unsigned grid = (unsigned)(need < a.max_blocks ? need : a.max_blocks);
   const bool q8 = a.fmt == MOEDC_FMT_Q8;
   switch (a.K) {
 #define MOEDC_LAUNCH(k, q)                                                     \
   if (!split)                                                                  \
-    combine_kernel<k, q, false, kWavesPerBlock><<<grid, 256, 0, s>>>(a);       \
+    combine_kernel<k, q, false, kWavesPerBlock, 1><<<grid, 256, 0, s>>>(a);    \
   else if (!wide)                                                              \
-    combine_kernel<k, q, true, kWavesPerBlock><<<grid, 256, 0, s>>>(a);        \
+    combine_kernel<k, q, true, kWavesPerBlock, 1><<<grid, 256, 0, s>>>(a);     \
   else                                                                         \
-    combine_kernel<k, q, true, 16><<<grid, 1024, 0, s>>>(a);
+    combine_kernel<k, q, true, 16, wide_chunks(k)><<<grid, 1024, 0, s>>>(a);
 #define MOEDC_CASE(k)          \
   case k:                      \
     if (q8) {                  \

@@ -509,6 +509,37 @@ def test_combine_limited_matches_combine(workgroups, fmt):
     assert np.array_equal(host_u16(y), want)
 
 
+@pytest.mark.parametrize("H,K", [(1152, 5), (640, 3), (1152, 15), (8192, 16), (128, 1), (4096, 13)])
+@pytest.mark.parametrize("T", [37, 300])
+def test_combine_limited_unit_shapes(H, K, T):
+    """Capped combine: multi-chunk units (a ragged last unit when the chunk
+    count is odd), single-chunk units from K = 14, dropped entries; both
+    formats against the oracle."""
+    rng = np.random.default_rng(H + 17 * K + T)
+    S = 97
+    wl = W.Workload("cl", "", T, H, K, K, K, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(K, S, np.int32), None, 3, "normal")
+    log(f"[case] combine_limited H={H} K={K} T={T}")
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    s = plan.sizes
+    ebuf = W.make_expert_out_bf16(H + K, s.total_slots, H)
+    xq = W.make_expert_out_bf16(H + K + 1, T, H)                 # BF16 rows to quantize
+    qslots = np.arange(T, dtype=np.int32).reshape(T, 1) % s.total_slots
+    dref = oracle.dispatch(oracle.Cfg(H, 1, 1, 1, 0, 1, [s.total_slots]), xq, qslots,
+                           s.total_slots, s.slot_stride)
+    slots = rng.integers(0, s.total_slots, (T, K)).astype(np.int32)
+    slots[rng.random((T, K)) < 0.15] = -1
+    w = W.make_gates(H + K + 2, T, K)
+    for fmt, src_host in ((M.FMT_BF16, ebuf), (M.FMT_Q8, dref)):
+        want = oracle.combine(cfg, src_host, fmt, slots, w)
+        src = dev_i16(src_host) if fmt == M.FMT_BF16 else dev(src_host)
+        for wgs in (1, 7):
+            y = torch.full((T, H), -1, dtype=torch.int16, device="cuda")
+            plan.combine_limited(src, fmt, dev(slots), dev(w), y, wgs)
+            assert np.array_equal(host_u16(y), want), (fmt, wgs)
+
+
 # ------------------------------------------------------------------ expert W8A8 GEMM
 
 def _gemm_case(wl, x, logits, seed=21):
