@@ -535,7 +535,8 @@ def summarize_rocprof(d, out):
     print(text)
 
 
-def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes,
+                   required=("combine", "dispatch", "route", "expert_gemm")):
     """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE runs,
     each counter scaled by what it reads for a plain copy of known size."""
     import csv
@@ -559,17 +560,24 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
                      f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
                      f"{copy_bytes}-byte copy); valid while source_sha matches."}
-    # Kernels of the global workload's launches (whole-token combine, BF16).
-    for key, tag in (("combine", "combine_kernel<8, false, false, 4>"),
+    # Kernels of the global workload's launches (whole-token combine, BF16);
+    # the tags are name prefixes, so extra trailing template arguments match.
+    missing = []
+    for key, tag in (("combine", "combine_kernel<8, false, false, 4"),
                      ("dispatch", "dispatch_kernel<14, false>"),
                      ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm<true>(")):
         kf = [k for k in fetch if tag in k]
         kw = [k for k in write if tag in k]
         if not kf or not kw:
+            missing.append(key)
             continue
         out[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]),
                     "fetch_bytes": fetch[kf[0]] * ff, "write_bytes": write[kw[0]] * fw,
                     "bytes_per_launch": fetch[kf[0]] * ff + write[kw[0]] * fw}
+    missing = [k for k in missing if k in required]
+    if missing:
+        raise SystemExit(f"record_traffic: no counter rows for {missing} in {fetch_dir} / "
+                         f"{write_dir}; nothing written")
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))

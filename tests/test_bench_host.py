@@ -6,6 +6,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -62,7 +64,7 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     tf = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, false, 4>(moedc::CombineArgs)"
+    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, false, 4, 1>(moedc::CombineArgs)"
     _write_csv(str(tmp_path / "f" / "f_counter_collection.csv"), hdr,
                [[name, "FETCH_SIZE", 1000.0], [name, "FETCH_SIZE", 1000.0]])
     _write_csv(str(tmp_path / "w" / "w_counter_collection.csv"), hdr, [[name, "WRITE_SIZE", 500.0]])
@@ -72,7 +74,7 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     _write_csv(str(tmp_path / "cw" / "c_counter_collection.csv"), hdr,
                [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 4.0]])
     bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
-                         str(tmp_path / "cw"), 4096)
+                         str(tmp_path / "cw"), 4096, required=("combine",))
     d = json.loads(tf.read_text())
     assert d["combine"]["fetch_bytes"] == 1000 * 1024 * 2.0
     assert d["combine"]["write_bytes"] == 500 * 1024 * 1.0
@@ -84,3 +86,9 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     d["combine"]["source_sha"] = "0" * 16
     tf.write_text(json.dumps(d))
     assert bench.measured_traffic("combine") is None
+    # A required kernel without counter rows is an error, and nothing is written.
+    tf.unlink()
+    with pytest.raises(SystemExit):
+        bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
+                             str(tmp_path / "cw"), 4096)
+    assert not tf.exists()
