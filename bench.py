@@ -424,6 +424,7 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, xd, slots, iters=5):
     plan_pt.bind_workspace(ws_pt)
     plan_pt.dispatch(xd, slots, dbuf)
     us_pt = timed(plan_pt, ws_pt)
+    lib_us = library_int8_gemm(wl, counts, dbuf, Wd, plan.sizes.slot_stride, iters)
     del Wd
     torch.cuda.empty_cache()
     tops, tops_pt = ops / (us * 1e-6) / 1e12, ops / (us_pt * 1e-6) / 1e12
@@ -432,7 +433,43 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, xd, slots, iters=5):
                          "unit": "TOP/s (int8)", "frac": tops / INT8_PEAK_TOPS,
                          "traffic": measured_traffic("expert_gemm")},
             "weight_GBps": P * H * H / (us * 1e-6) / 1e9,
-            "per_token_scales": {"us": us_pt, "TOPs": tops_pt, "frac": tops_pt / INT8_PEAK_TOPS}}
+            "per_token_scales": {"us": us_pt, "TOPs": tops_pt, "frac": tops_pt / INT8_PEAK_TOPS},
+            "library_int8_gemm": {
+                "what": "torch._int_mm (hipBLASLt) once per expert on the same rows and weights, "
+                        "int32 out, no scales: context, not part of the path",
+                "us": lib_us, "frac": ops / (lib_us * 1e-6) / 1e12 / INT8_PEAK_TOPS}}
+
+
+def library_int8_gemm(wl, counts, dbuf, Wd, slot_stride, iters):
+    """The library's int8 GEMM on the expert layer's shapes: for each physical
+    expert, its occupied rows (INT8 payload copied out of the dispatch slots,
+    untimed) times its weight matrix, as 256 back-to-back torch._int_mm
+    calls."""
+    import numpy as np
+    import torch
+    H = wl.hidden
+    n = np.minimum(counts.cpu().numpy(), wl.capacity)
+    base = np.concatenate([[0], np.cumsum(wl.capacity)[:-1]])
+    rows = torch.from_numpy(np.concatenate([base[p] + np.arange(n[p]) for p in range(len(n))])).cuda()
+    xq = dbuf.view(-1, slot_stride)[rows, :H].contiguous()  # [used][H] int8
+    xq = xq.view(torch.int8)
+    out = torch.empty((xq.shape[0], H), dtype=torch.int32, device="cuda")
+    starts = np.concatenate([[0], np.cumsum(n)])
+    parts = [(xq[starts[p]:starts[p + 1]], Wd[p].t(), out[starts[p]:starts[p + 1]])
+             for p in range(len(n)) if n[p] > 16]
+
+    def run():
+        for a, b, o in parts:
+            torch._int_mm(a, b, out=o)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / iters
 
 
 def placement(workers=8, redundant=32, max_replicas=8):
