@@ -280,6 +280,44 @@ def test_slots_outside_the_buffer_are_skipped(T):
         assert np.array_equal(host_u16(y), ref), f"fmt {fmt}"
 
 
+def test_bf16_rounding_every_upper_half_and_rounding_class():
+    """The device's fp32 -> BF16 rounding, reached through the Q8 combine with
+    payload q = 1, gate 1.0 and one entry per token: every output is
+    bf16(fma(1, s, +0)) of its group's fp32 scale s.  The scales take every
+    one of the 2^16 upper halves (each sign, exponent -- zero, subnormal,
+    normal, Inf, NaN -- and upper mantissa) with eight lower halves (0, 1,
+    0x4000, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF), which covers every case
+    of round-to-nearest-even: below, at and above the halfway point, with an
+    even or odd kept bit.  Expected values are the oracle's, whose rounding
+    is defined by exact distances, not bit tricks.  Rows after y stay
+    untouched."""
+    H, G = 8192, 64
+    lows = np.array([0x0000, 0x0001, 0x4000, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF], np.uint32)
+    x = ((np.arange(1 << 16, dtype=np.uint32)[:, None] << 16) | lows[None, :]).ravel()
+    T = x.size // G                                              # 8192 tokens
+    wl = W.Workload("bf16", "", T, H, 1, 1, 1, 0, W.SCORE_SIGMOID_NORM,
+                    np.array([T], np.int32), None, 0, "normal")
+    log(f"[case] bf16 rounding over {x.size} scales")
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    s = plan.sizes
+    dbuf = np.zeros((s.total_slots, s.slot_stride), np.uint8)
+    dbuf[:, :H] = 1                                              # q = 1 everywhere
+    dbuf[:T, H:H + 4 * G] = x.reshape(T, G).view(np.uint8)
+    slots = np.arange(T, dtype=np.int32).reshape(T, 1)
+    w = np.ones((T, 1), np.float32)
+    want = oracle.combine(cfg, dbuf, M.FMT_Q8, slots, w)
+    guard = 16
+    ybuf = torch.full((T + guard, H), 0x5A5A, dtype=torch.int16, device="cuda")
+    plan.combine(dev(dbuf), M.FMT_Q8, dev(slots), dev(w), ybuf[:T])
+    torch.cuda.synchronize()
+    got = host_u16(ybuf[:T])
+    assert np.array_equal(got, want)
+    assert bool((ybuf[T:] == 0x5A5A).all()), "combine wrote past y"
+    # every group's 128 outputs are the rounding of one scale: spot-check the layout
+    assert np.array_equal(got[:, ::128].ravel(), want[:, ::128].ravel())
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_combine_parity_full_size(name):
     wl, x, logits, plan, cfg = setup(name)
