@@ -8,9 +8,9 @@
 //
 //  1. topk_wave: one wave per token spread over many CUs.  Each lane holds
 //     the logits of experts lane, lane+64, ...; K rounds of a wave-wide
-//     argmax over (value desc, id asc) pick the experts in order, then the
-//     gates and the physical ids (replica copy t mod r_e, shared expert
-//     last) are written.
+//     argmax over (value desc, id asc) pick the experts in order, lane j
+//     keeping pick j; lane j then evaluates pick j's gate and physical id
+//     (replica copy t mod r_e, shared expert last) and writes them.
 //  2. rank_dispatch: one block per token.  Every block rebuilds per-expert
 //     token bit masks from the T x K ids in LDS (a few KB from L2), so the
 //     rank of token t at expert p -- the number of lower tokens that chose
@@ -25,13 +25,13 @@
 // Up to kOneLaunchTokens tokens (one per wave of a block) both entries are a
 // single launch instead: every block runs the whole batch's top-k itself
 // and goes straight on to its ranks, which saves a launch and a round trip
-// through memory.  A wave's top-k of one token takes a few microseconds of
-// dependent cross-lane steps, so beyond one token per wave the two-launch
-// path is faster (measured: 6.4 against 7.5 us for 1 token, 22 against
-// 9.7 us for 96).  Picks, counts, offsets,
-// slots and dispatched bytes equal those of the large-batch kernels bit for
-// bit; sigmoid gates too (same per-token arithmetic), while a softmax
-// denominator is summed in another order (within the stated gate tolerance).
+// through memory.  A wave's top-k of one token is ~1.7 us of dependent
+// cross-lane steps (K rounds of ~460 cycles), so beyond one token per wave
+// the two-launch path is faster (at 96 tokens the one-launch form measured
+// 22 us against 9.7).  Picks, counts, offsets, slots and dispatched bytes
+// equal those of the large-batch kernels bit for bit; sigmoid gates too
+// (same per-token arithmetic), while a softmax denominator is summed in
+// another order (within the stated gate tolerance).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
