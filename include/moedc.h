@@ -66,12 +66,12 @@ typedef enum moedc_elem_fmt {
  * redundant copies of popular experts, one expert per simulated rank).
  */
 typedef struct moedc_config {
-  int32_t max_tokens;          /* largest token count any call will pass (>= 0) */
+  int32_t max_tokens;          /* largest token count any call will pass, 0..2^24 */
   int32_t hidden;              /* H: multiple of 128, 128..8192 */
   int32_t group_size;          /* values per fp32 scale: 128, or hidden (one scale per token) */
   int32_t num_logical_experts; /* E_log: logits per token, 1..1024 */
   int32_t num_phys_experts;    /* E_phys: physical experts incl. replicas and shared, 1..1024 */
-  int32_t top_k;               /* routed picks per token, 1..E_log */
+  int32_t top_k;               /* routed picks per token, 1..E_log; top_k + num_shared <= 16 */
   int32_t num_shared;          /* 0 or 1; the shared expert is physical id E_phys-1 */
   int32_t score_fn;            /* moedc_score_fn */
   int32_t max_replicas;        /* R: columns of replica_table, 1..8 */
