@@ -53,9 +53,34 @@ def algorithmic_bytes(T, H, K, E):
     )
 
 
+def code_text(src):
+    """C/C++ source without comments and with whitespace runs collapsed:
+    what the compiler sees, so editing a comment keeps recorded counters."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            i = src.find("\n", i)
+            i = n if i < 0 else i
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":  # string or character literal, kept verbatim
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def measured_traffic(kernel):

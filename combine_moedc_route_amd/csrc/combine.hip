@@ -11,13 +11,14 @@
 // the number of workgroups.  A unit is a whole token on large batches, or
 // one 512-value chunk of a token on small ones (below kSplitTokens tokens),
 // so a decode batch of ~100 tokens still spreads over every CU; under a
-// workgroup cap the workgroups grow to 16 waves.  A unit's
-// values are covered in groups of CH 512-value chunks (lane l holds values
-// 512c + 8l .. +8 of chunk c).  Within a group the wave walks the K expert rows in route
-// order and, for each row, issues the loads of all kChunks chunks back to
-// back: a contiguous 7 KiB (BF16) run of one row instead of 1 KiB pieces of
-// K rows in turn, which keeps HBM row-buffer locality on a gather whose rows
-// are scattered over the slot buffer.  Expert rows and the output are
+// workgroup cap the workgroups grow to 16 waves and their units to
+// wide_chunks(K) chunks.  A unit's values are covered in groups of CH
+// 512-value chunks (lane l holds values 512c + 8l .. +8 of chunk c).
+// Within a group the wave walks the K expert rows in route order and, for
+// each row, issues the loads of all CH chunks back to back: on large
+// batches a contiguous 7 KiB (BF16) run of one row instead of 1 KiB pieces
+// of K rows in turn, which keeps HBM row-buffer locality on a gather whose
+// rows are scattered over the slot buffer.  Expert rows and the output are
 // touched once, so loads and stores carry the non-temporal hint.  A dropped
 // entry (slot -1), like any slot outside the plan's buffer, loads nothing
 // and contributes fma(0, 0, acc) = acc exactly.

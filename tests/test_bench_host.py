@@ -92,3 +92,16 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
         bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
                              str(tmp_path / "cw"), 4096)
     assert not tf.exists()
+
+
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = 'int a = 1; // note\n/* block */ const char *s = "// kept"; float b = a / 2.0f;\n'
+    (tmp_path / "k.hip").write_text(src)
+    h = bench.source_sha("k.hip")
+    (tmp_path / "k.hip").write_text(src.replace("note", "another note").replace("block", "x"))
+    assert bench.source_sha("k.hip") == h            # comments only
+    (tmp_path / "k.hip").write_text(src.replace('"// kept"', '"// changed"'))
+    assert bench.source_sha("k.hip") != h            # a string literal is code
+    (tmp_path / "k.hip").write_text(src.replace("a / 2.0f", "a * 2.0f"))
+    assert bench.source_sha("k.hip") != h
