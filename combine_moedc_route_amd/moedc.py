@@ -144,6 +144,17 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need(t, what: str, n: int = 0, nbytes: int = 0, itemsize: int = 0):
+    """Refuse a tensor that is too small for what the call will write or read
+    (the C ABI sees only its address), or of the wrong element size."""
+    if itemsize and t.element_size() != itemsize:
+        raise ValueError(f"{what}: {itemsize}-byte elements expected, got {t.dtype}")
+    if n and t.numel() < n:
+        raise ValueError(f"{what}: needs {n} elements, has {t.numel()}")
+    if nbytes and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: needs {nbytes} bytes, has {t.numel() * t.element_size()}")
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -244,13 +255,34 @@ class Plan:
         self.bind_workspace(bufs["workspace"])
         return bufs
 
+    def _route_bufs(self, T, topk_ids, topk_w, counts, offsets, slots, dropped, workspace):
+        K, P = self.K, self.num_phys
+        _need(topk_ids, "topk_ids", T * K, itemsize=4)
+        _need(topk_w, "topk_w", T * K, itemsize=4)
+        _need(counts, "counts", P, itemsize=4)
+        _need(offsets, "offsets", P + 1, itemsize=4)
+        _need(slots, "slots", T * K, itemsize=4)
+        _need(dropped, "dropped", 1, itemsize=4)
+        _need(workspace, "workspace", nbytes=self.sizes.workspace_bytes)
+
+    def _combine_bufs(self, T, expert_out, fmt, slots, topk_w, y):
+        s = self.sizes
+        _need(expert_out, "expert_out",
+              nbytes=s.dispatch_buf_bytes if fmt == FMT_Q8 else s.combine_buf_bytes)
+        _need(slots, "slots", T * self.K, itemsize=4)
+        _need(topk_w, "topk_w", T * self.K, itemsize=4)
+        _need(y, "y", T * self.hidden, itemsize=2)
+
     def bind_workspace(self, ws, stream=None):
+        _need(ws, "workspace", nbytes=self.sizes.workspace_bytes)
         _check(lib().moedc_plan_bind_workspace(self._h, _ptr(ws), _stream(stream)),
                "moedc_plan_bind_workspace")
 
     def route(self, logits, topk_ids, topk_w, counts, offsets, slots, dropped,
               workspace, num_tokens: Optional[int] = None, stream=None):
         T = logits.shape[0] if num_tokens is None else num_tokens
+        _need(logits, "logits", T * self.num_logical, itemsize=4)
+        self._route_bufs(T, topk_ids, topk_w, counts, offsets, slots, dropped, workspace)
         _check(lib().moedc_route(self._h, T, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
                                  _ptr(counts), _ptr(offsets), _ptr(slots), _ptr(dropped),
                                  _ptr(workspace), _stream(stream)), "moedc_route")
@@ -258,18 +290,26 @@ class Plan:
     def dispatch(self, x, slots, dispatch_buf, num_tokens: Optional[int] = None,
                  stream=None):
         T = x.shape[0] if num_tokens is None else num_tokens
+        _need(x, "x", T * self.hidden, itemsize=2)
+        _need(slots, "slots", T * self.K, itemsize=4)
+        _need(dispatch_buf, "dispatch_buf", nbytes=self.sizes.dispatch_buf_bytes)
         _check(lib().moedc_dispatch(self._h, T, _ptr(x), _ptr(slots), _ptr(dispatch_buf),
                                     _stream(stream)), "moedc_dispatch")
 
     def combine(self, expert_out, fmt: int, slots, topk_w, y,
                 num_tokens: Optional[int] = None, stream=None):
         T = y.shape[0] if num_tokens is None else num_tokens
+        self._combine_bufs(T, expert_out, fmt, slots, topk_w, y)
         _check(lib().moedc_combine(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
                                    _ptr(topk_w), _ptr(y), _stream(stream)), "moedc_combine")
 
     def route_dispatch(self, logits, x, topk_ids, topk_w, counts, offsets, slots, dropped,
                        dispatch_buf, workspace, num_tokens: Optional[int] = None, stream=None):
         T = logits.shape[0] if num_tokens is None else num_tokens
+        _need(logits, "logits", T * self.num_logical, itemsize=4)
+        _need(x, "x", T * self.hidden, itemsize=2)
+        _need(dispatch_buf, "dispatch_buf", nbytes=self.sizes.dispatch_buf_bytes)
+        self._route_bufs(T, topk_ids, topk_w, counts, offsets, slots, dropped, workspace)
         _check(lib().moedc_route_dispatch(
             self._h, T, _ptr(logits), _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(counts),
             _ptr(offsets), _ptr(slots), _ptr(dropped), _ptr(dispatch_buf), _ptr(workspace),
@@ -278,17 +318,30 @@ class Plan:
     def combine_limited(self, expert_out, fmt: int, slots, topk_w, y, max_workgroups: int,
                         num_tokens: Optional[int] = None, stream=None):
         T = y.shape[0] if num_tokens is None else num_tokens
+        self._combine_bufs(T, expert_out, fmt, slots, topk_w, y)
         _check(lib().moedc_combine_limited(self._h, T, _ptr(expert_out), fmt, _ptr(slots),
                                            _ptr(topk_w), _ptr(y), max_workgroups,
                                            _stream(stream)), "moedc_combine_limited")
 
     def expert_w8a8(self, counts, dispatch_buf, weights, w_scale, combine_buf, workspace,
                     stream=None):
+        s, H, P = self.sizes, self.hidden, self.num_phys
+        _need(counts, "counts", P, itemsize=4)
+        _need(dispatch_buf, "dispatch_buf", nbytes=s.dispatch_buf_bytes)
+        _need(weights, "weights", P * H * H, itemsize=1)
+        _need(w_scale, "w_scale", P * H, itemsize=4)
+        _need(combine_buf, "combine_buf", nbytes=s.combine_buf_bytes)
+        _need(workspace, "workspace", nbytes=s.workspace_bytes)
         _check(lib().moedc_expert_w8a8(self._h, _ptr(counts), _ptr(dispatch_buf), _ptr(weights),
                                        _ptr(w_scale), _ptr(combine_buf), _ptr(workspace),
                                        _stream(stream)), "moedc_expert_w8a8")
 
     def expert_stub(self, counts, dispatch_buf, combine_buf, workspace, stream=None):
+        s = self.sizes
+        _need(counts, "counts", self.num_phys, itemsize=4)
+        _need(dispatch_buf, "dispatch_buf", nbytes=s.dispatch_buf_bytes)
+        _need(combine_buf, "combine_buf", nbytes=s.combine_buf_bytes)
+        _need(workspace, "workspace", nbytes=s.workspace_bytes)
         _check(lib().moedc_expert_stub(self._h, _ptr(counts), _ptr(dispatch_buf),
                                        _ptr(combine_buf), _ptr(workspace),
                                        _stream(stream)), "moedc_expert_stub")

@@ -140,6 +140,47 @@ def test_call_validation_returns_before_launch():
     L.moedc_plan_destroy(None)
 
 
+def test_binding_refuses_undersized_or_mistyped_tensors():
+    """The C ABI sees only addresses, so the binding checks each tensor's
+    element size and extent against the plan before the call (the checks
+    run before the device check, so CPU tensors exercise them)."""
+    import torch
+    wl = W.get("tiny")
+    p = M.Plan.from_workload(wl)
+    T, K, P, H, E = wl.tokens, wl.K, wl.num_phys, wl.hidden, wl.num_logical
+    s = p.sizes
+    i32, f32 = dict(dtype=torch.int32), dict(dtype=torch.float32)
+
+    def route_args(**over):
+        a = dict(logits=torch.empty((T, E), **f32), topk_ids=torch.empty((T, K), **i32),
+                 topk_w=torch.empty((T, K), **f32), counts=torch.empty(P, **i32),
+                 offsets=torch.empty(P + 1, **i32), slots=torch.empty((T, K), **i32),
+                 dropped=torch.empty(1, **i32),
+                 workspace=torch.empty(s.workspace_bytes, dtype=torch.uint8))
+        a.update(over)
+        return a
+
+    with pytest.raises(ValueError, match="libmoedc takes device tensors"):
+        p.route(**route_args())                  # sizes pass, then the device check
+    for name, bad in [("offsets", torch.empty(P, **i32)),
+                      ("slots", torch.empty((T, K - 1), **i32)),
+                      ("workspace", torch.empty(s.workspace_bytes - 1, dtype=torch.uint8)),
+                      ("topk_w", torch.empty((T, K), dtype=torch.float16))]:
+        with pytest.raises(ValueError, match=name):
+            p.route(**route_args(**{name: bad}))
+    with pytest.raises(ValueError, match="dispatch_buf"):
+        p.dispatch(torch.empty((T, H), dtype=torch.int16), torch.empty((T, K), **i32),
+                   torch.empty(s.dispatch_buf_bytes - 512, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="expert_out"):
+        p.combine(torch.empty(s.combine_buf_bytes - 2, dtype=torch.uint8), M.FMT_BF16,
+                  torch.empty((T, K), **i32), torch.empty((T, K), **f32),
+                  torch.empty((T, H), dtype=torch.int16))
+    with pytest.raises(ValueError, match="^y: needs"):
+        p.combine(torch.empty(s.combine_buf_bytes, dtype=torch.uint8), M.FMT_BF16,
+                  torch.empty((T + 1, K), **i32), torch.empty((T + 1, K), **f32),
+                  torch.empty((T, H), dtype=torch.int16), num_tokens=T + 1)
+
+
 def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(M, "_lib", None)
