@@ -16,9 +16,9 @@
 // value's quotient x/scale is the correctly rounded fp32 quotient, obtained
 // from one IEEE reciprocal per group plus an fma correction.  The wave then
 // writes the token's payload (8 bytes per lane, 512 contiguous bytes per
-// store instruction) and its scales (one dword per lane) into each of the
-// K slots, with the non-temporal hint (slots are written once and read by
-// a later kernel).  Entries with slot -1 (dropped), or any slot outside the
+// store instruction) and its scales (one dword per lane, zero words after
+// them up to a 128-byte boundary) into each of the K slots, with the
+// non-temporal hint (slots are written once and read by a later kernel).  Entries with slot -1 (dropped), or any slot outside the
 // plan's buffer, are skipped.  Many waves per CU overlap one token's loads with other
 // tokens' quantize and store phases.
 //
@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
   }
 
   const int32_t *srow = a.slots + t * a.K;
+  const int sw = scale_words(a.G);
   for (int k = 0; k < a.K; ++k) {
     const int slot = uniform(srow[k]);
     if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
@@ -92,7 +93,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs a) {
         __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
       }
     }
-    if (lane < a.G) __builtin_nontemporal_store(my_scale, reinterpret_cast<float *>(dst + H + 4 * lane));
+    if (lane < sw)
+      __builtin_nontemporal_store(lane < a.G ? my_scale : 0.0f,
+                                  reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 
@@ -113,6 +116,8 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
   const uint32_t m = row16_max_u32(absmax8(v));
   const float sc = __uint_as_float(m << 16) / 127.0f;
   const uint2 q = quant8(v, sc);
+  // The chunk-0 wave also writes the zero words after the last scale.
+  const bool pad = c == 0 && lane >= a.G && lane < scale_words(a.G);
   for (int k = 0; k < a.K; ++k) {
     const int slot = __builtin_amdgcn_readlane(my_slot, k);
     if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
@@ -122,6 +127,7 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
       __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
       if ((lane & 15) == 0) __builtin_nontemporal_store(sc, reinterpret_cast<float *>(dst + H + 4 * (e >> 7)));
     }
+    if (pad) __builtin_nontemporal_store(0.0f, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 

@@ -329,11 +329,13 @@ __device__ __forceinline__ void store_token(const DispatchArgs &da, const uint4 
   }
   const float s = __uint_as_float(m << 16) / 127.0f;
   const uint2 q = quant8(v, s);
-  if (e < H) {
-    for (int k = 0; k < da.K; ++k) {
-      const int slot = slot_of[k];
-      if (slot < 0) continue;
-      uint8_t *dst = da.dbuf + (int64_t)slot * da.slot_stride;
+  // Wave 0 also writes the zero words after the last scale.
+  const bool pad = wave == 0 && lane >= da.G && lane < scale_words(da.G);
+  for (int k = 0; k < da.K; ++k) {
+    const int slot = slot_of[k];
+    if (slot < 0) continue;
+    uint8_t *dst = da.dbuf + (int64_t)slot * da.slot_stride;
+    if (e < H) {
       const u32x2 qq = {q.x, q.y};
       __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
       if (PER_TOKEN) {
@@ -342,6 +344,7 @@ __device__ __forceinline__ void store_token(const DispatchArgs &da, const uint4 
         __builtin_nontemporal_store(s, reinterpret_cast<float *>(dst + H + 4 * (e >> 7)));
       }
     }
+    if (pad) __builtin_nontemporal_store(0.0f, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 

@@ -156,8 +156,10 @@ moedc_status moedc_route(const moedc_plan *plan, int32_t num_tokens,
  * clamp(round-half-even(x / scale), -127, 127) with a correctly rounded
  * fp32 quotient (scale 0 gives q 0).  Slot s occupies bytes
  * [s*slot_stride, (s+1)*slot_stride) of dispatch_buf: INT8 payload at
- * [0, H), G fp32 scales (little-endian) at [H, H + 4*G); the rest of the
- * slot and slots no token maps to are not written.  Entries with slot -1
+ * [0, H), G fp32 scales (little-endian) at [H, H + 4*G), then zero bytes
+ * up to the next multiple of 128, H + 4*round_up(G, 32) (so no slot ends
+ * inside a 128-byte line); the rest of the slot and slots no token maps to
+ * are not written.  Entries with slot -1
  * (dropped) are skipped, and so is any slot outside [0, total_slots), so a
  * corrupt slot table cannot make the kernel write outside dispatch_buf.
  * x: BF16 [num_tokens][H] (16-byte aligned); slots: from moedc_route;

@@ -108,15 +108,40 @@ def check_dispatch_tokens(dbuf, x_bits, slots, tokens, H, group_size=128):
     return len(rows)
 
 
-def check_dispatch_untouched(dbuf, slots, H, sentinel=SENTINEL, group_size=128):
-    """Unoccupied slots and slot tails keep the sentinel."""
+def scale_region_end(H, group_size=128):
+    """End of the bytes dispatch writes in a slot: the G scales, then zero
+    bytes up to the next multiple of 128 (the slot layout in moedc.h)."""
     G = H // group_size
+    return H + 4 * (-(-G // 32) * 32)
+
+
+def expected_dispatch_buffer(cfg, x, slots, sizes, fill=SENTINEL):
+    """The whole dispatch buffer a call on a `fill`-initialised buffer must
+    leave: the oracle's payload and scales (the method's bytes) in every
+    occupied slot, the layout's zero padding after the scales, and `fill`
+    everywhere else."""
+    ref = np.full((sizes.total_slots, sizes.slot_stride), fill, np.uint8)
+    oracle.dispatch(cfg, x, slots, sizes.total_slots, sizes.slot_stride, buf=ref)
+    H, G = cfg.hidden, cfg.hidden // cfg.group_size
+    occupied = np.unique(slots[(slots >= 0) & (slots < sizes.total_slots)])
+    ref[occupied, H + 4 * G:scale_region_end(H, cfg.group_size)] = 0
+    return ref
+
+
+def check_dispatch_untouched(dbuf, slots, H, sentinel=SENTINEL, group_size=128):
+    """Unoccupied slots keep the sentinel.  In an occupied slot the bytes
+    after the G scales are zero up to the next multiple of 128 (the header's
+    layout: H + 4 * round_up(G, 32)) and the rest keeps the sentinel."""
+    G = H // group_size
+    end = scale_region_end(H, group_size)
+    assert end % 128 == 0 and end - (H + 4 * G) < 128
     S = dbuf.shape[0]
     occ = torch.zeros(S, dtype=torch.bool, device="cuda")
     sl = torch.from_numpy(slots[slots >= 0].astype(np.int64)).cuda()
     occ[sl] = True
     assert bool((dbuf[~occ] == sentinel).all()), "unoccupied slot written"
-    assert bool((dbuf[occ, H + 4 * G:] == sentinel).all()), "slot tail written"
+    assert bool((dbuf[occ, H + 4 * G:end] == 0).all()), "scale padding not zero"
+    assert bool((dbuf[occ, end:] == sentinel).all()), "slot tail written"
 
 
 def ulp_diff_bf16(a_bits, b_bits):

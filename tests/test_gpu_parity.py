@@ -14,6 +14,7 @@ from combine_moedc_route_amd import workloads as W
 
 from gpu_common import (SENTINEL, U, bf16_to_f32, check_dispatch_tokens,
                         check_dispatch_untouched, compare_route, dev, dev_i16,
+                        expected_dispatch_buffer,
                         gpu_dispatch, gpu_route, host_u16, log, sample_tokens,
                         ulp_diff_bf16)
 
@@ -131,10 +132,9 @@ def test_dispatch_parity(name):
     n = check_dispatch_tokens(dbuf, x, r["slots"], np.arange(x.shape[0]), wl.hidden,
                               wl.group_size)
     check_dispatch_untouched(dbuf, r["slots"], wl.hidden, group_size=wl.group_size)
-    # Whole-buffer byte equality against the oracle's own dispatch.
-    s = plan.sizes
-    ref = np.full((s.total_slots, s.slot_stride), SENTINEL, np.uint8)
-    oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride, buf=ref)
+    # Whole-buffer byte equality against the oracle's own dispatch (plus the
+    # slot layout's zero padding after the scales).
+    ref = expected_dispatch_buffer(cfg, x, r["slots"], plan.sizes)
     assert np.array_equal(dbuf.cpu().numpy(), ref)
     log(f"  {n} slots bit-exact")
 
@@ -505,8 +505,7 @@ def _fused_case(wl, logits, x):
     got["dropped"] = int(got["dropped"][0])
     want = oracle.route(cfg, logits)
     compare_route(wl, got, want)
-    ref = np.full((s.total_slots, s.slot_stride), SENTINEL, np.uint8)
-    oracle.dispatch(cfg, x, want["slots"], s.total_slots, s.slot_stride, buf=ref)
+    ref = expected_dispatch_buffer(cfg, x, want["slots"], s)
     assert np.array_equal(dbuf.cpu().numpy(), ref)
     return got
 
