@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
   const uint32_t m = row16_max_u32(absmax8(v));
   const float sc = __uint_as_float(m << 16) / 127.0f;
   const uint2 q = quant8(v, sc);
-  // The chunk-0 wave also writes the zero words after the last scale.
-  const bool pad = c == 0 && lane >= a.G && lane < scale_words(a.G);
+  float word;
+  const bool has_word = chunk_scale_word(c, nch, a.G, sc, lane, &word);
   for (int k = 0; k < a.K; ++k) {
     const int slot = __builtin_amdgcn_readlane(my_slot, k);
     if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
@@ -125,9 +125,8 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
     if (e < H) {
       const u32x2 qq = {q.x, q.y};
       __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
-      if ((lane & 15) == 0) __builtin_nontemporal_store(sc, reinterpret_cast<float *>(dst + H + 4 * (e >> 7)));
     }
-    if (pad) __builtin_nontemporal_store(0.0f, reinterpret_cast<float *>(dst + H + 4 * lane));
+    if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 

@@ -311,9 +311,11 @@ __global__ __launch_bounds__(kBlock) void rank_single(RouteArgs a) {
 
 // Quantize and store one token after its slots are in slot_of[]: wave c
 // holds values 512 c .. 512 c + 511 in v (called by the whole block).
+// chunk_lds: 64 words of LDS for the chunks' maxima (one scale per token)
+// or the groups' scales.
 template <bool PER_TOKEN>
 __device__ __forceinline__ void store_token(const DispatchArgs &da, const uint4 &v,
-                                            const int *slot_of, uint32_t *chunk_max) {
+                                            const int *slot_of, uint32_t *chunk_lds) {
   const int wave = uniform(threadIdx.x >> 6), lane = lane_id();
   const int H = da.H;
   const int e = wave * 512 + lane * 8;
@@ -321,16 +323,27 @@ __device__ __forceinline__ void store_token(const DispatchArgs &da, const uint4 
   if (PER_TOKEN) {
     m = max(m, (uint32_t)__shfl_xor((int)m, 16));
     m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-    if (lane == 0) chunk_max[wave] = m;
+    if (lane == 0) chunk_lds[wave] = m;
     __syncthreads();
     m = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < kBlock / 64; ++w2) m = max(m, chunk_max[w2]);
+    for (int w2 = 0; w2 < kBlock / 64; ++w2) m = max(m, chunk_lds[w2]);
   }
   const float s = __uint_as_float(m << 16) / 127.0f;
   const uint2 q = quant8(v, s);
-  // Wave 0 also writes the zero words after the last scale.
-  const bool pad = wave == 0 && lane >= da.G && lane < scale_words(da.G);
+  // Scale words with their zero padding, as one store of whole 128-byte
+  // lines per slot: wave 0 stores the token's one scale and the zeros after
+  // it; with 128-value groups the chunks' scales are gathered in LDS and
+  // the last wave stores them all (instead of 16 bytes from each chunk's
+  // wave: 3-5% faster from 64 tokens up).
+  float word = lane == 0 ? s : 0.0f;
+  bool has_word = PER_TOKEN && wave == 0 && lane < scale_words(1);
+  if (!PER_TOKEN) {
+    if ((lane & 15) == 0 && e < H) chunk_lds[e >> 7] = __float_as_uint(s);
+    __syncthreads();
+    word = lane < da.G ? __uint_as_float(chunk_lds[lane]) : 0.0f;
+    has_word = wave == kBlock / 64 - 1 && lane < scale_words(da.G);
+  }
   for (int k = 0; k < da.K; ++k) {
     const int slot = slot_of[k];
     if (slot < 0) continue;
@@ -338,13 +351,8 @@ __device__ __forceinline__ void store_token(const DispatchArgs &da, const uint4 
     if (e < H) {
       const u32x2 qq = {q.x, q.y};
       __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
-      if (PER_TOKEN) {
-        if (wave == 0 && lane == 0) __builtin_nontemporal_store(s, reinterpret_cast<float *>(dst + H));
-      } else if ((lane & 15) == 0) {
-        __builtin_nontemporal_store(s, reinterpret_cast<float *>(dst + H + 4 * (e >> 7)));
-      }
     }
-    if (pad) __builtin_nontemporal_store(0.0f, reinterpret_cast<float *>(dst + H + 4 * lane));
+    if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 
@@ -353,7 +361,7 @@ template <bool PER_TOKEN>
 __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchArgs da) {
   __shared__ RankLds L;
   __shared__ int slot_of[kMaxK];
-  __shared__ uint32_t chunk_max[kBlock / 64];
+  __shared__ uint32_t chunk_lds[64];  // store_token's exchange
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   int id[kIdsPerThread];
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kBlock) void rank_dispatch(RouteArgs ra, DispatchAr
     ra.slots[(int64_t)t * ra.K + tid] = slot;
   }
   __syncthreads();
-  store_token<PER_TOKEN>(da, v, slot_of, chunk_max);
+  store_token<PER_TOKEN>(da, v, slot_of, chunk_lds);
 }
 
 // ---- 3. one launch for batches of at most kOneLaunchTokens tokens ----------
@@ -415,7 +423,7 @@ struct OneLds {
   RankLds L;
   int ids[kOneLaunchTokens][kMaxK];
   int slot_of[kMaxK];
-  uint32_t chunk_max[kBlock / 64];
+  uint32_t chunk_lds[64];  // store_token's exchange
 };
 
 // moedc_route: block 0 writes every token's outputs and slots, block 1
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(kBlock) void route_dispatch_one(RouteArgs ra, Dispa
     ra.slots[(int64_t)t * ra.K + tid] = slot;
   }
   __syncthreads();
-  store_token<PER_TOKEN>(da, v, S.slot_of, S.chunk_max);
+  store_token<PER_TOKEN>(da, v, S.slot_of, S.chunk_lds);
 }
 
 template <int NV>

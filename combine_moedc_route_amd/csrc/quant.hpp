@@ -16,6 +16,19 @@ namespace moedc {
 // 2.7% of dispatch time at H = 7168) than the up to 124 padding bytes cost.
 __device__ __forceinline__ int scale_words(int G) { return (G + 31) & ~31; }
 
+// Scale word `lane` of a slot as the wave of 512-value chunk c of nch
+// stores it, from its per-group scales sc (DPP row r holds group 4c + r):
+// the chunk's own groups, and in the last chunk also the zero words after
+// group G - 1, so the padding adds no store instruction.  Returns whether
+// this lane stores; *val is the word.  Called by the whole wave.
+__device__ __forceinline__ bool chunk_scale_word(int c, int nch, int G, float sc, int lane,
+                                                 float *val) {
+  const float own = __shfl(sc, ((lane - 4 * c) & 3) * 16);
+  *val = lane < G ? own : 0.0f;
+  return (lane >= 4 * c && lane < min(4 * c + 4, G)) ||
+         (c == nch - 1 && lane >= G && lane < scale_words(G));
+}
+
 // Max of |x| over 8 BF16 values as a BF16 magnitude bit pattern.
 __device__ __forceinline__ uint32_t absmax8(const uint4 &v) {
   const uint32_t a0 = v.x & 0x7FFF7FFFu, a1 = v.y & 0x7FFF7FFFu;
