@@ -34,11 +34,15 @@ INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA
 METRIC = ("dispatch+combine µs and tokens/s at 30720×7168 top-8/256; "
           "% of HBM peak GB/s")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+# Every source a kernel is compiled from: its .hip file and the headers it
+# includes (moedc.h through internal.hpp).
+_CSRC = "combine_moedc_route_amd/csrc/"
+_COMMON = (_CSRC + "device.hpp", _CSRC + "internal.hpp", "include/moedc.h")
 KERNEL_SOURCES = {
-    "combine": "combine_moedc_route_amd/csrc/combine.hip",
-    "dispatch": "combine_moedc_route_amd/csrc/dispatch.hip",
-    "route": "combine_moedc_route_amd/csrc/route.hip",
-    "expert_gemm": "combine_moedc_route_amd/csrc/expert_gemm.hip",
+    "combine": (_CSRC + "combine.hip",) + _COMMON,
+    "dispatch": (_CSRC + "dispatch.hip", _CSRC + "quant.hpp") + _COMMON,
+    "route": (_CSRC + "route.hip",) + _COMMON,
+    "expert_gemm": (_CSRC + "expert_gemm.hip",) + _COMMON,
 }
 
 
@@ -78,20 +82,28 @@ def code_text(src):
     return " ".join("".join(out).split())
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
-        return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
+def source_sha(rels):
+    """Hash of the code (comments and whitespace removed) of the files
+    `rels` (one path or several)."""
+    h = hashlib.sha256()
+    for rel in ([rels] if isinstance(rels, str) else rels):
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode() + b"\0")
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload="global"):
     """HBM bytes per launch from committed PMC runs, or None if the kernel
-    source changed since they were taken."""
+    source changed since they were taken or they were taken on another
+    workload (the bytes of a launch depend on its shape)."""
     try:
         with open(TRAFFIC_FILE) as f:
             d = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
         return None
     if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    if d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -251,7 +263,7 @@ def run(args):
     # Dominant kernel: the one with the larger mean duration.
     dom = "combine" if mean(c_us) >= mean(d_us) else "dispatch"
     dom_bytes, dom_gbps = (cb, comb_gbps) if dom == "combine" else (ab["dispatch"], disp_gbps)
-    traffic = measured_traffic(dom) if fmt == M.FMT_BF16 else None
+    traffic = measured_traffic(dom, wl.name) if fmt == M.FMT_BF16 else None
     res = {
         "metric": METRIC,
         "value": T / (ms_per_step * 1e-3),
@@ -633,7 +645,7 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
         if not kf or not kw:
             missing.append(key)
             continue
-        out[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]),
+        out[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]), "workload": "global",
                     "fetch_bytes": fetch[kf[0]] * ff, "write_bytes": write[kw[0]] * fw,
                     "bytes_per_launch": fetch[kf[0]] * ff + write[kw[0]] * fw}
     missing = [k for k in missing if k in required]

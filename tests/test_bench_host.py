@@ -82,6 +82,9 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert "dispatch" not in d
     # The recorded figure is served while the kernel source is unchanged...
     assert bench.measured_traffic("combine") == 1000 * 1024 * 2.0 + 500 * 1024
+    # ...for the workload the counters were taken on only...
+    assert d["combine"]["workload"] == "global"
+    assert bench.measured_traffic("combine", "prefill") is None
     # ...and withheld once it changes.
     d["combine"]["source_sha"] = "0" * 16
     tf.write_text(json.dumps(d))
@@ -105,3 +108,18 @@ def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.source_sha("k.hip") != h            # a string literal is code
     (tmp_path / "k.hip").write_text(src.replace("a / 2.0f", "a * 2.0f"))
     assert bench.source_sha("k.hip") != h
+
+
+def test_source_hash_covers_every_file_of_a_kernel(tmp_path, monkeypatch):
+    """A record is keyed to the kernel's .hip file and the headers it
+    includes: a code change in a header invalidates it too."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "k.hip").write_text("int main_part = 1;\n")
+    (tmp_path / "h.hpp").write_text("int helper = 2;\n")
+    h = bench.source_sha(("k.hip", "h.hpp"))
+    assert h != bench.source_sha("k.hip")
+    (tmp_path / "h.hpp").write_text("int helper = 3;\n")
+    assert bench.source_sha(("k.hip", "h.hpp")) != h
+    for key, files in bench.KERNEL_SOURCES.items():
+        assert "combine_moedc_route_amd/csrc/internal.hpp" in files, key
+    assert "combine_moedc_route_amd/csrc/quant.hpp" in bench.KERNEL_SOURCES["dispatch"]
