@@ -113,9 +113,10 @@ moedc_status moedc_plan_sizes(const moedc_plan *plan, moedc_sizes *out);
 /* Uploads the plan's static tables (capacities, slot bases, replica table)
  * into the caller's device workspace of workspace_bytes (16-byte aligned),
  * asynchronously on `stream`.  Needed once per workspace before route,
- * route_dispatch, the expert layer or the expert stand-in use it.  Calls
- * that share a workspace must not overlap (route and the expert layer keep
- * per-call work lists in it). */
+ * route_dispatch, the expert layer or the expert stand-in use it.  The
+ * copies read the plan's own host memory: keep the plan alive until they
+ * have run on `stream`.  Calls that share a workspace must not overlap
+ * (route and the expert layer keep per-call work lists in it). */
 moedc_status moedc_plan_bind_workspace(const moedc_plan *plan, void *workspace,
                                        hipStream_t stream);
 
