@@ -1,4 +1,5 @@
-"""HIP-graph capture of the decode step through the C ABI.
+"""HIP-graph capture of the decode step, and of a large-batch step with
+the expert layer, through the C ABI.
 
 The benchmark times the 96-token decode path as graph replays, so this test
 captures moedc_route_dispatch + the stand-in expert + moedc_combine (and,
@@ -6,6 +7,8 @@ separately, the two-step moedc_route + moedc_dispatch + moedc_combine) in a
 graph, replays it several times with eager work and synchronisations in
 between, and checks every replay bit for bit against an eager run, which
 itself is checked against the oracle."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -73,6 +76,64 @@ def test_decode_step_graph_replays_match_eager(fused):
         for k in ("topk_ids", "slots", "counts", "offsets"):
             b[k].fill_(-3)
         b["topk_w"].fill_(-3.0)
+        y.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from the eager run"
+    log("  4 replays bit-identical to the eager step")
+
+
+def test_large_batch_step_with_expert_layer_graph_replays_match_eager():
+    """The large-batch path in a graph: 3000 tokens (three route kernels,
+    whole-token dispatch and combine) and the W8A8 expert layer between
+    dispatch and combine, whose tile list is rebuilt on the device from
+    the route's counts on every replay."""
+    # capacity 470 per expert against a mean of 450 entries: a few drops
+    wl = dataclasses.replace(W.with_tokens(W.get("ragged"), 3000),
+                             capacity=np.full(40, 470, np.int32))
+    log(f"[case] large-batch graph T={wl.tokens} H={wl.hidden} P={wl.num_phys}")
+    plan, b, x, logits, xd, lg, y = _state(wl)
+    Wt, wsc = W.make_expert_weights(7, wl.num_phys, wl.hidden)
+    Wd, wsd = torch.from_numpy(Wt).cuda(), torch.from_numpy(wsc).cuda()
+    rargs = (b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"], b["dropped"])
+
+    def step():
+        plan.route(lg, *rargs, b["workspace"])
+        plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+        plan.expert_w8a8(b["counts"], b["dispatch_buf"], Wd, wsd, b["combine_buf"], b["workspace"])
+        plan.combine(b["combine_buf"], M.FMT_BF16, b["slots"], b["topk_w"], y)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {"ids": b["topk_ids"].clone(), "w": b["topk_w"].clone(),
+                "slots": b["slots"].clone(), "counts": b["counts"].clone(),
+                "offsets": b["offsets"].clone(), "dropped": b["dropped"].clone(),
+                "y": y.clone()}
+
+    step()
+    ref = snapshot()
+    cfg = oracle.Cfg.from_workload(wl)
+    want = oracle.route(cfg, logits)
+    assert np.array_equal(ref["ids"].cpu().numpy(), want["topk_ids"])
+    assert np.array_equal(ref["slots"].cpu().numpy(), want["slots"])
+    assert int(ref["dropped"].item()) == want["dropped"] > 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for k in ("topk_ids", "slots", "counts", "offsets", "dropped"):
+            b[k].fill_(-3)
+        b["topk_w"].fill_(-3.0)
+        b["combine_buf"].fill_(-3)
         y.fill_(-3)
         torch.cuda.synchronize()
         g.replay()
