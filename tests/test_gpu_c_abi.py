@@ -1,7 +1,10 @@
 """The C ABI used from C++ alone: tests/c/abi_driver (built by
 __graft_entry__.build()) allocates its buffers with hipMalloc, runs route ->
-dispatch -> stand-in expert -> combine on a small seeded layer and checks
-the layout invariants and the argument checks.  Started as a child process."""
+dispatch -> stand-in expert -> combine and the fused route + dispatch on
+three small seeded layers (128-value scales; one scale per token with a
+shared expert and replicas; a one-launch decode batch with softmax gates)
+and checks the layout invariants, the fused call's equality with the two
+calls, and the argument checks.  Started as a child process."""
 import os
 import subprocess
 
