@@ -14,8 +14,8 @@
 //   y[t][n] = bf16(acc * w_scale[p][n])
 // (a group is 128 inputs, or the whole row with one scale per token).
 //
-// Work list: the route's counts give each expert ceil(rows/128) row tiles
-// and ceil(H/256) channel tiles.  A band is kBandTiles channel tiles x all
+// Work list: the route's counts give each expert ceil(rows / tile rows) row
+// tiles and ceil(H/256) channel tiles.  A band is kBandTiles channel tiles x all
 // row tiles of one expert (32 tiles for 8 row tiles), ordered row-major so
 // that neighbouring entries share a weight slice or a slot tile.  Bands are
 // dealt round-robin to the 8 XCDs; workgroup b runs on XCD b mod 8 (the
@@ -26,13 +26,19 @@
 // of once per tile.  The placement is only a performance assumption: any
 // placement computes the same result.
 //
-// Per tile, 8 waves (2 token halves x 4 channel quarters, 64 x 64 each); MFMA
+// Per tile, 8 waves (2 token halves x 4 channel quarters); MFMA
 // v_mfma_i32_16x16x64_i8 with A = 16 weight rows (channels) and B = 16 slot
 // rows (tokens), so each lane ends up with 4 consecutive channels of one
 // token (8-byte BF16 stores).  K advances 128 inputs per step; slot rows and
 // weight rows are shared by 4 and 2 waves respectively and pass through a
 // double-buffered LDS tile, loaded one step ahead into registers, with one
-// barrier per step.  A tile moves 48 KiB per step for 8.4 MOP (175 op/B).
+// barrier per step.  With 128-input groups a tile is 128 slot rows x 256
+// channels (waves of 64 x 64) and moves 48 KiB per step for 8.4 MOP
+// (175 op/B).  With one scale per token the int32 sums span the whole row
+// and are scaled once in the epilogue, so the registers that would hold
+// fp32 partial sums hold a second 64 tokens instead: 256 x 256 tiles (waves
+// of 128 tokens x 64 channels), 64 KiB per step for 16.8 MOP (262 op/B),
+// a quarter fewer LDS reads per MFMA and half the tiles and barriers.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -42,7 +48,8 @@ namespace moedc {
 
 namespace {
 
-constexpr int BM = 128;   // slot rows (tokens) per tile
+constexpr int BM = 128;   // slot rows (tokens) per tile with 128-input groups
+constexpr int BM_PT = 256;  // with one scale per token
 constexpr int BN = kGemmChannels;  // output channels per tile
 constexpr int BK = 128;   // inputs per K step
 
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
     if (j < a.J && k < a.P * a.nbe) {
       const int p = k / a.nbe, b = k % a.nbe;
       const int rows = min(a.counts[p], a.cap[p]);
-      tiles = (rows + BM - 1) / BM * min(kBandTiles, a.ntiles - b * kBandTiles);
+      tiles = (rows + a.bm - 1) / a.bm * min(kBandTiles, a.ntiles - b * kBandTiles);
     }
     int incl = tiles;
 #pragma unroll
@@ -86,28 +93,27 @@ __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
   }
 }
 
-// Loads of K step g: 16 KiB of weights (4 x 16 B per thread, rows n, n+32,
-// n+64, n+96), 8 KiB of slot payload (2 x 16 B; rows past the expert's
-// tokens read as zero) and, at the first step of a scale group, one
-// activation scale per slot row.
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
-// One K step of the tile, as loaded by one thread: 2 x 16 B of slot rows
-// (rows r and r+64), 4 x 16 B of weight rows (r, r+64, r+128, r+192) and, at
-// the first step of a scale group, one activation scale (threads < BM).
-// Rows past the expert's tokens or past H channels read as zero.
+// One K step of the tile, as loaded by one thread: XR x 16 B of slot rows
+// (rows r, r+64, ...; XR = tile rows / 64), 4 x 16 B of weight rows (r,
+// r+64, r+128, r+192) and, at the first step of a scale group, one
+// activation scale (threads below the tile rows).  Rows past the expert's
+// tokens or past H channels read as zero.
+template <int XR>
 struct StepRegs {
-  v4i x[2], w[4];
+  v4i x[XR], w[4];
   float s;
 };
 
-__device__ __forceinline__ StepRegs fetch_step(const GemmArgs &a, const int8_t *wtile,
-                                               int64_t slot0, int rows, int chans, int g,
-                                               int spg, int tid) {
+template <int XR>
+__device__ __forceinline__ StepRegs<XR> fetch_step(const GemmArgs &a, const int8_t *wtile,
+                                                   int64_t slot0, int rows, int chans, int g,
+                                                   int spg, int tid) {
   const int r = tid >> 3, c = 16 * (tid & 7);
-  StepRegs st;
+  StepRegs<XR> st;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < XR; ++i) {
     const int t = r + 64 * i;
     st.x[i] = t < rows ? ld16(a.dbuf + (slot0 + t) * a.slot_stride + g * BK + c)
                        : v4i{0, 0, 0, 0};
@@ -118,7 +124,7 @@ __device__ __forceinline__ StepRegs fetch_step(const GemmArgs &a, const int8_t *
     st.w[i] = n < chans ? ld16(wtile + (int64_t)n * a.H + g * BK + c) : v4i{0, 0, 0, 0};
   }
   st.s = 0.0f;
-  if (tid < BM && g % spg == 0 && tid < rows)
+  if (tid < 64 * XR && g % spg == 0 && tid < rows)
     st.s = *reinterpret_cast<const float *>(a.dbuf + (slot0 + tid) * a.slot_stride + a.H +
                                             4 * (g / spg));
   return st;
@@ -127,15 +133,16 @@ __device__ __forceinline__ StepRegs fetch_step(const GemmArgs &a, const int8_t *
 // Scales are double-buffered by group parity: group j's scale is written
 // with its first step and read after its last, while group j+1's goes to
 // the other buffer.
-__device__ __forceinline__ void stage(int8_t (&Xs)[BM][BK], int8_t (&Ws)[BN][BK],
-                                      float (&sx)[2][BM], const StepRegs &st, int g, int spg,
-                                      int tid) {
+template <int XR>
+__device__ __forceinline__ void stage(int8_t (&Xs)[64 * XR][BK], int8_t (&Ws)[BN][BK],
+                                      float (&sx)[2][64 * XR], const StepRegs<XR> &st, int g,
+                                      int spg, int tid) {
   const int r = tid >> 3, c = tid & 7;  // rows r + 64 i keep r's low 3 bits
 #pragma unroll
-  for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][swz(r, c)]) = st.x[i];
+  for (int i = 0; i < XR; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][swz(r, c)]) = st.x[i];
 #pragma unroll
   for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i *>(&Ws[r + 64 * i][swz(r, c)]) = st.w[i];
-  if (tid < BM && g % spg == 0) sx[(g / spg) & 1][tid] = st.s;
+  if (tid < 64 * XR && g % spg == 0) sx[(g / spg) & 1][tid] = st.s;
 }
 
 // G128: every K step is one 128-input scale group, so the first MFMA of a
@@ -143,9 +150,12 @@ __device__ __forceinline__ void stage(int8_t (&Xs)[BM][BK], int8_t (&Ws)[BN][BK]
 // into fp32 at the end of the same step.  Otherwise one scale spans the row.
 template <bool G128>
 __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BM][BK];
+  constexpr int TB = G128 ? BM : BM_PT;  // tile rows
+  constexpr int TF = TB / 32;            // 16-token blocks per wave
+  constexpr int XR = TB / 64;            // slot-row loads per thread and step
+  __shared__ __attribute__((aligned(16))) int8_t Xs[2][TB][BK];
   __shared__ __attribute__((aligned(16))) int8_t Ws[2][BN][BK];
-  __shared__ float sx[2][BM];
+  __shared__ float sx[2][TB];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -172,25 +182,30 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
     const int w = min(kBandTiles, a.ntiles - band * kBandTiles);
     const int mt = off / w, nt = band * kBandTiles + off % w;
     const int used = min(a.counts[p], a.cap[p]);
-    const int rows = min(BM, used - mt * BM);
+    const int rows = min(TB, used - mt * TB);
     const int chans = min(BN, H - nt * BN);
-    const int64_t slot0 = (int64_t)a.capbase[p] + (int64_t)mt * BM;
+    const int64_t slot0 = (int64_t)a.capbase[p] + (int64_t)mt * TB;
     const int8_t *wtile = a.W + ((int64_t)p * H + (int64_t)nt * BN) * H;
 
-    v4i acc[4][4];
-    float accf[4][4][4];
+    // With one scale per token the int32 sums span the whole row and are
+    // scaled once in the epilogue; fp32 accumulators exist only for groups.
+    v4i acc[4][TF];
+    float accf[4][G128 ? TF : 1][4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
+      for (int tf = 0; tf < TF; ++tf) {
         acc[nf][tf] = v4i{0, 0, 0, 0};
+        if (G128) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) accf[nf][tf][q] = 0.0f;
+          for (int q = 0; q < 4; ++q) accf[nf][tf][q] = 0.0f;
+        }
       }
 
     __syncthreads();  // the previous tile's last reads of the LDS tiles are done
-    stage(Xs[0], Ws[0], sx, fetch_step(a, wtile, slot0, rows, chans, 0, spg, tid), 0, spg, tid);
-    StepRegs nxt = fetch_step(a, wtile, slot0, rows, chans, min(1, ksteps - 1), spg, tid);
+    stage<XR>(Xs[0], Ws[0], sx, fetch_step<XR>(a, wtile, slot0, rows, chans, 0, spg, tid), 0, spg,
+              tid);
+    StepRegs<XR> nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, min(1, ksteps - 1), spg, tid);
 
     // Waves 4-7 (the second wave on each SIMD) fold a step's group sums
     // after the next barrier, while waves 0-3 run that step's MFMAs, and run
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
         for (int tf = 0; tf < 4; ++tf) sv[tf] = sx[(g - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
       }
       __syncthreads();  // step g staged by all; step g-1's reads of buf^1 done
-      if (lag && g > 0) {
+      if (G128 && lag && g > 0) {
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf)
 #pragma unroll
@@ -216,40 +231,43 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        v4i av[4], bv[4];
+        v4i av[4];
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf)
           av[nf] = *reinterpret_cast<const v4i *>(
               &Ws[buf][64 * wn + 16 * nf + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
+        // Token fragments four at a time (16 registers live, not 4 TF).
 #pragma unroll
-        for (int tf = 0; tf < 4; ++tf)
-          bv[tf] = *reinterpret_cast<const v4i *>(
-              &Xs[buf][64 * wm + 16 * tf + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
+        for (int t0 = 0; t0 < TF; t0 += 4) {
+          v4i bv[4];
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
+          for (int i = 0; i < 4; ++i)
+            bv[i] = *reinterpret_cast<const v4i *>(
+                &Xs[buf][16 * TF * wm + 16 * (t0 + i) + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
 #pragma unroll
-          for (int tf = 0; tf < 4; ++tf)
-            acc[nf][tf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                av[nf], bv[tf], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][tf], 0, 0, 0);
+          for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[nf][t0 + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  av[nf], bv[i], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][t0 + i], 0, 0, 0);
+        }
       }
-      if (g + 1 < ksteps) stage(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
-      if (g + 2 < ksteps) nxt = fetch_step(a, wtile, slot0, rows, chans, g + 2, spg, tid);
+      if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
+      if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
 
-      if (!lag && g % spg == spg - 1) {  // end of an activation-scale group
+      if (G128 && !lag) {  // end of the step's scale group
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf) {
-          const float s = sx[(g / spg) & 1][64 * wm + 16 * tf + (lane & 15)];
+          const float s = sx[g & 1][64 * wm + 16 * tf + (lane & 15)];
 #pragma unroll
-          for (int nf = 0; nf < 4; ++nf) {
+          for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               accf[nf][tf][q] = __builtin_fmaf(s, (float)acc[nf][tf][q], accf[nf][tf][q]);
-            if (!G128) acc[nf][tf] = v4i{0, 0, 0, 0};
-          }
         }
       }
     }
-    if (lag) {  // the last step's fold (its scales are not restaged before the next tile)
+    if (G128 && lag) {  // the last step's fold (its scales are not restaged before the next tile)
 #pragma unroll
       for (int tf = 0; tf < 4; ++tf) {
         const float s = sx[(ksteps - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
       }
     }
 
-    // ---- epilogue: lane holds channels n0..n0+3 of token 64 wm + 16 tf + lane%16 ----
+    // ---- epilogue: lane holds channels n0..n0+3 of token 16 TF wm + 16 tf + lane%16 ----
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
       const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
@@ -269,11 +287,20 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
       const int n0 = nt * BN + nl;
       const float4 ws = *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H + n0);
 #pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        const int t = 64 * wm + 16 * tf + (lane & 15);
+      for (int tf = 0; tf < TF; ++tf) {
+        const int t = 16 * TF * wm + 16 * tf + (lane & 15);
         if (t < rows) {
-          const uint2 o = make_uint2(pack_bf16x2(accf[nf][tf][0] * ws.x, accf[nf][tf][1] * ws.y),
-                                     pack_bf16x2(accf[nf][tf][2] * ws.z, accf[nf][tf][3] * ws.w));
+          float v[4];
+          if (G128) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = accf[nf][G128 ? tf : 0][q];
+          } else {  // the one group's fold: fma(s, isum, +0)
+            const float s = sx[0][t];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(s, (float)acc[nf][tf][q], 0.0f);
+          }
+          const uint2 o = make_uint2(pack_bf16x2(v[0] * ws.x, v[1] * ws.y),
+                                     pack_bf16x2(v[2] * ws.z, v[3] * ws.w));
           *reinterpret_cast<uint2 *>(a.ebuf + (slot0 + t) * (int64_t)H + n0) = o;
         }
       }
@@ -283,8 +310,10 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_expert_gemm(const GemmArgs &a, int grid, hipStream_t s) {
-  if (a.J > 1024 || grid % kXcds) return hipErrorInvalidValue;
+hipError_t launch_expert_gemm(const GemmArgs &args, int grid, hipStream_t s) {
+  if (args.J > 1024 || grid % kXcds) return hipErrorInvalidValue;
+  GemmArgs a = args;
+  a.bm = a.steps_per_group == 1 ? BM : BM_PT;  // the tile rows of the kernel below
   gemm_tiles<<<1, 1024, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

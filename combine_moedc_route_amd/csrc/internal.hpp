@@ -103,6 +103,7 @@ struct GemmArgs {
   int32_t H, P, ntiles, steps_per_group;
   int32_t nbe;              // bands per expert: ceil(ntiles / kBandTiles)
   int32_t J;                // bands per XCD: ceil(P * nbe / kXcds)
+  int32_t bm;               // slot rows per tile (set by the launcher)
 };
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t s);
