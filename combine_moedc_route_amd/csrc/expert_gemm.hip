@@ -280,29 +280,45 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
     }
 
     // ---- epilogue: lane holds channels n0..n0+3 of token 16 TF wm + 16 tf + lane%16 ----
+    // Token rows one after another: the four 32-byte stores that make up a
+    // row's 128-byte line issue back to back and the line reaches memory
+    // whole (channel-major order left lines partly written in L2: up to
+    // 1.85x the output bytes written).  Weight scales load at each store
+    // with 128-input groups and once per tile with one scale per token (the
+    // register allocation that ran faster for each).
+    float4 ws[4];
+    if (!G128) {
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-      const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
-      if (nl >= chans) continue;
-      const int n0 = nt * BN + nl;
-      const float4 ws = *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H + n0);
+      for (int nf = 0; nf < 4; ++nf) {
+        const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
+        ws[nf] = nl < chans ? *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H +
+                                                                 nt * BN + nl)
+                            : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
 #pragma unroll
-      for (int tf = 0; tf < TF; ++tf) {
-        const int t = 16 * TF * wm + 16 * tf + (lane & 15);
-        if (t < rows) {
-          float v[4];
-          if (G128) {
+    for (int tf = 0; tf < TF; ++tf) {
+      const int t = 16 * TF * wm + 16 * tf + (lane & 15);
+      if (t >= rows) continue;
+      const float s = G128 ? 0.0f : sx[0][t];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = accf[nf][G128 ? tf : 0][q];
-          } else {  // the one group's fold: fma(s, isum, +0)
-            const float s = sx[0][t];
+      for (int nf = 0; nf < 4; ++nf) {
+        const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
+        if (nl >= chans) continue;
+        const int64_t n0 = (int64_t)nt * BN + nl;
+        const float4 w4 =
+            G128 ? *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H + n0) : ws[nf];
+        float v[4];
+        if (G128) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(s, (float)acc[nf][tf][q], 0.0f);
-          }
-          const uint2 o = make_uint2(pack_bf16x2(v[0] * ws.x, v[1] * ws.y),
-                                     pack_bf16x2(v[2] * ws.z, v[3] * ws.w));
-          *reinterpret_cast<uint2 *>(a.ebuf + (slot0 + t) * (int64_t)H + n0) = o;
+          for (int q = 0; q < 4; ++q) v[q] = accf[nf][G128 ? tf : 0][q];
+        } else {  // the one group's fold: fma(s, isum, +0)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(s, (float)acc[nf][tf][q], 0.0f);
         }
+        const uint2 o = make_uint2(pack_bf16x2(v[0] * w4.x, v[1] * w4.y),
+                                   pack_bf16x2(v[2] * w4.z, v[3] * w4.w));
+        *reinterpret_cast<uint2 *>(a.ebuf + (slot0 + t) * (int64_t)H + n0) = o;
       }
     }
   }
