@@ -615,8 +615,13 @@ def test_expert_w8a8_parity_per_token(H, T):
     _gemm_case(wl, x, logits)
 
 
-def test_expert_w8a8_full_size_sampled():
+@pytest.mark.parametrize("group", [128, 7168])   # 128 x 256 tiles; 256 x 256 (one scale per token)
+def test_expert_w8a8_full_size_sampled(group):
     wl, x, logits, plan, cfg = setup("global")
+    if group != wl.group_size:
+        wl = dataclasses.replace(wl, group_size=group)
+        plan, cfg = M.Plan.from_workload(wl), oracle.Cfg.from_workload(wl)
+    log(f"[case] expert layer, global batch, group {group}")
     s = plan.sizes
     H, P = wl.hidden, wl.num_phys
     r = oracle.route(cfg, logits)
