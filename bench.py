@@ -684,7 +684,7 @@ def main():
         summarize_rocprof(args.summarize_rocprof, args.out)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU (the MoE path's simulated "
+        print("bench.py: libmoedc runs on exactly one GPU (the MoE path's simulated "
               "expert-parallel ranks are partitions of one GPU's HBM); --gpus must be 1.",
               file=sys.stderr, flush=True)
         sys.exit(2)
