@@ -61,7 +61,7 @@ def random_case(seed):
     return wl, x, np.ascontiguousarray(logits, np.float32), kind
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_random_config_full_path(seed):
     wl, x, logits, kind = random_case(seed)
     T, H, K = wl.tokens, wl.hidden, wl.K
