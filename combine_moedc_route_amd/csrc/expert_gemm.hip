@@ -229,6 +229,14 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
             for (int q = 0; q < 4; ++q)
               accf[nf][tf][q] = __builtin_fmaf(sv[tf], (float)acc[nf][tf][q], accf[nf][tf][q]);
       }
+      // Stage step g+1 into the other buffer (free since this barrier) and
+      // issue step g+2's loads: before this step's MFMAs with 128-input
+      // groups, which gives the loads a whole step of lead (1.5% faster),
+      // after them with one scale per token (as fast or faster there).
+      if (G128) {
+        if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
+        if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         v4i av[4];
@@ -252,8 +260,10 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
                   av[nf], bv[i], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][t0 + i], 0, 0, 0);
         }
       }
-      if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
-      if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
+      if (!G128) {
+        if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
+        if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
+      }
 
       if (G128 && !lag) {  // end of the step's scale group
 #pragma unroll
