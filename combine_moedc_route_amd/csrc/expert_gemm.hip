@@ -237,6 +237,10 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
         if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
         if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
       }
+      // Raised wave priority while a wave issues its MFMAs, so the SIMD's
+      // other wave (staging, loads, folds) does not delay them (2% faster
+      // with one scale per token, neutral with groups).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         v4i av[4];
@@ -260,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
                   av[nf], bv[i], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][t0 + i], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (!G128) {
         if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
         if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
