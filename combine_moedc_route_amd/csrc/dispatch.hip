@@ -22,9 +22,10 @@
 // plan's buffer, are skipped.  Many waves per CU overlap one token's loads with other
 // tokens' quantize and store phases.
 //
-// Small batches (below kSplitTokens tokens, 128-value groups) use one wave
-// per 512-value chunk of a token instead, so ~100 decode tokens still keep
-// every CU busy; the bytes written are the same.
+// Small batches (below kSplitTokens tokens) use one wave per 512-value chunk
+// of a token instead (with one scale per token, a workgroup per token whose
+// waves share the token's amax through LDS), so ~100 decode tokens still
+// keep every CU busy; the bytes written are the same.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -130,10 +131,55 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
   }
 }
 
+// Small batches with one scale per token: one 16-wave workgroup per token,
+// wave c holding chunk c; the token's amax is a workgroup max through LDS.
+// (A wave per whole token leaves a decode batch on ~100 waves: 2.2x slower.)
+__global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
+  __shared__ uint32_t wave_max[16];
+  __shared__ int slot_of[kMaxK];
+  const int t = blockIdx.x;
+  const int wave = uniform(threadIdx.x >> 6), lane = lane_id();
+  const int H = a.H;
+  const int e = wave * 512 + lane * 8;
+  if ((int)threadIdx.x < a.K) {
+    const int s = a.slots[(int64_t)t * a.K + threadIdx.x];
+    slot_of[threadIdx.x] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
+  }
+  const uint4 v = e < H ? reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H)[wave * 64 + lane]
+                        : make_uint4(0, 0, 0, 0);
+  uint32_t m = row16_max_u32(absmax8(v));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  if (lane == 0) wave_max[wave] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) m = max(m, wave_max[w]);
+  const float sc = __uint_as_float(m << 16) / 127.0f;
+  const uint2 q = quant8(v, sc);
+  // Wave 0 stores the scale and the zero words after it (one line).
+  const bool has_word = wave == 0 && lane < scale_words(1);
+  const float word = lane == 0 ? sc : 0.0f;
+  for (int k = 0; k < a.K; ++k) {
+    const int slot = slot_of[k];
+    if (slot < 0) continue;  // dropped, or outside the buffer
+    uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
+    if (e < H) {
+      const u32x2 qq = {q.x, q.y};
+      __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst + e));
+    }
+    if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.T < kSplitTokens && a.per_token) {
+    dispatch_token_block<<<(unsigned)a.T, 1024, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.T < kSplitTokens && !a.per_token) {
     const int nch = (a.H + 511) / 512;
     const int64_t units = (int64_t)a.T * nch;
