@@ -592,6 +592,29 @@ def summarize_rocprof(d, out):
             lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                          f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
                          f"{float(r['Percentage']):6.2f}  {r['Name'][:110]}")
+        # Kernels launched with several grid sizes (one kernel serving the
+        # global and the decode batch): one row per launch shape, from the trace.
+        trace = path.replace("kernel_stats.csv", "kernel_trace.csv")
+        if os.path.exists(trace):
+            shapes = {}
+            with open(trace) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+                    shapes.setdefault(key, []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            names = {}
+            for (k, g, w) in shapes:
+                names[k] = names.get(k, 0) + 1
+            multi = sorted(key for key in shapes if names[key[0]] > 1 and "moedc::" in key[0])
+            if multi:
+                lines.append("# per launch shape (kernels launched with several grid sizes): "
+                             + os.path.relpath(trace, d))
+                lines.append(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} "
+                             f"{'threads':>10} {'wg':>5}  kernel")
+                for (k, g, w) in multi:
+                    v = shapes[(k, g, w)]
+                    lines.append(f"{len(v):6d} {statistics.fmean(v):10.2f} {min(v):10.2f} "
+                                 f"{max(v):10.2f} {g:10d} {w:5d}  {k[:110]}")
     for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         lines.append(f"# counters: {os.path.relpath(path, d)}")
         agg = {}

@@ -123,3 +123,20 @@ def test_source_hash_covers_every_file_of_a_kernel(tmp_path, monkeypatch):
     for key, files in bench.KERNEL_SOURCES.items():
         assert "combine_moedc_route_amd/csrc/internal.hpp" in files, key
     assert "combine_moedc_route_amd/csrc/quant.hpp" in bench.KERNEL_SOURCES["dispatch"]
+
+
+def test_summary_splits_a_kernel_launched_with_several_grid_sizes(tmp_path):
+    """One kernel serving two batch sizes gets one row per launch shape."""
+    name = "void moedc::(anonymous namespace)::dispatch_token_block<false>(moedc::DispatchArgs)"
+    _write_csv(str(tmp_path / "p" / "b_kernel_stats.csv"),
+               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+               [[name, 3, 1000.0, 4000.0, 430000.0, 100.0]])
+    hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X"]
+    _write_csv(str(tmp_path / "p" / "b_kernel_trace.csv"), hdr,
+               [[name, 0, 430000, 27525120, 896], [name, 0, 4000, 86016, 896],
+                [name, 0, 6000, 86016, 896]])
+    bench.summarize_rocprof(str(tmp_path / "p"), str(tmp_path / "s.txt"))
+    text = (tmp_path / "s.txt").read_text()
+    assert "per launch shape" in text
+    assert "     1     430.00     430.00     430.00   27525120   896" in text
+    assert "     2       5.00       4.00       6.00      86016   896" in text
