@@ -8,20 +8,19 @@
 // order, dropped entries skipped; BF16 round-to-nearest-even at the end.
 //
 // Mapping: a wave per work unit, a grid-stride loop when the caller caps
-// the number of workgroups.  A unit is a whole token on large batches, or
-// one 512-value chunk of a token on small ones (below kSplitTokens tokens),
-// so a decode batch of ~100 tokens still spreads over every CU; under a
-// workgroup cap the workgroups grow to 16 waves and their units to
-// wide_chunks(K) chunks.  A unit's values are covered in groups of CH
-// 512-value chunks (lane l holds values 512c + 8l .. +8 of chunk c).
-// Within a group the wave walks the K expert rows in route order and, for
-// each row, issues the loads of all CH chunks back to back: on large
-// batches a contiguous 7 KiB (BF16) run of one row instead of 1 KiB pieces
-// of K rows in turn, which keeps HBM row-buffer locality on a gather whose
-// rows are scattered over the slot buffer.  Expert rows and the output are
-// touched once, so loads and stores carry the non-temporal hint.  A dropped
-// entry (slot -1), like any slot outside the plan's buffer, loads nothing
-// and contributes fma(0, 0, acc) = acc exactly.
+// the number of workgroups.  A unit is one 512-value chunk of a token (lane
+// l holds values 512c + 8l .. +8), so a token's K expert rows are read by
+// its ceil(H/512) chunk waves at once: on a 30720-token batch, with 16-wave
+// workgroups, 7% faster than one wave per token walking each row in 7 KiB
+// runs, and a decode batch of ~100 tokens (4-wave workgroups) still spreads
+// over every CU.  Under a workgroup cap the workgroups have 16 waves and,
+// below 2048 tokens, units of wide_chunks(K) chunks.
+// A unit's wave loads the token's slots and gates together, then for each
+// expert row in route order issues the loads of its chunks back to back.
+// Expert rows and the output are touched once, so loads and stores carry
+// the non-temporal hint.  A dropped entry (slot -1), like any slot outside
+// the plan's buffer, loads nothing and contributes fma(0, 0, acc) = acc
+// exactly.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -31,9 +30,8 @@ namespace moedc {
 
 namespace {
 
-constexpr int kWavesPerBlock = 4;
-constexpr int kChunks = 7;  // 512-value chunks per group: 7168 = 2 groups
-constexpr int kSplitTokens = 2048;  // below this, one unit per 512-value chunk
+constexpr int kWavesPerBlock = 4;  // below kWideTokens: spread over every CU
+constexpr int kWideTokens = 2048;   // from here on, 16-wave workgroups
 // Chunks per unit under a workgroup cap: 2 (twice the loads in flight per
 // wave), 1 from K = 14 on, where two chunks' loads no longer fit in the
 // 128 registers of a 16-wave workgroup.
@@ -63,29 +61,17 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
   const int H = a.H;
   int slot[K];  // -1 for an entry that is skipped
   float w[K];
-  if (CH < kChunks) {
-    // Chunk units (small batches, latency-bound): all 2K loads of the
-    // token's slots and gates are issued before any is used, one memory
-    // latency instead of K dependent ones.
+  // All 2K loads of the token's slots and gates are issued before any is
+  // used: one memory latency instead of K dependent ones.
 #pragma unroll
-    for (int k = 0; k < K; ++k) slot[k] = a.slots[t * K + k];
+  for (int k = 0; k < K; ++k) slot[k] = a.slots[t * K + k];
 #pragma unroll
-    for (int k = 0; k < K; ++k) w[k] = a.w[t * K + k];
+  for (int k = 0; k < K; ++k) w[k] = a.w[t * K + k];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int s = uniform(slot[k]);
-      slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
-      w[k] = slot[k] >= 0 ? w[k] : 0.0f;
-    }
-  } else {
-    // Whole tokens (large batches, many waves per CU hide the latency):
-    // gates of skipped entries are not read.
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int s = uniform(a.slots[t * K + k]);
-      slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
-      w[k] = slot[k] >= 0 ? a.w[t * K + k] : 0.0f;
-    }
+  for (int k = 0; k < K; ++k) {
+    const int s = uniform(slot[k]);
+    slot[k] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
+    w[k] = slot[k] >= 0 ? w[k] : 0.0f;
   }
   uint16_t *yrow = a.y + t * H;
   const int hend = min(H, 512 * c1);  // values of this unit end here
@@ -147,26 +133,23 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
   }
 }
 
-// SPLIT: units are UC consecutive 512-value chunks of a token; otherwise
-// whole tokens.  WPB waves per workgroup (16 when the caller caps the
-// workgroup count, so the few CUs it gets still hold many loads in flight;
-// their units are then wide_chunks(K) chunks).
-template <int K, bool Q8, bool SPLIT, int WPB, int UC>
+// Units of UC consecutive 512-value chunks of a token; WPB waves per
+// workgroup (16 when the caller caps the workgroup count, so the few CUs it
+// gets still hold many loads in flight; their units are then
+// wide_chunks(K) chunks).
+template <int K, bool Q8, int WPB, int UC>
 __global__ __launch_bounds__(64 * WPB) void combine_kernel(CombineArgs a) {
   const int lane = lane_id();
   const int nch = (a.H + 511) / 512;
-  const int nu = (nch + UC - 1) / UC;  // units per token when SPLIT
-  const int64_t units = SPLIT ? (int64_t)a.T * nu : a.T;
+  const int nu = (nch + UC - 1) / UC;  // units per token
+  const int64_t units = (int64_t)a.T * nu;
   const int64_t stride = (int64_t)gridDim.x * WPB;
   for (int64_t u = (int64_t)blockIdx.x * WPB + uniform(threadIdx.x >> 6); u < units;
        u += stride) {
-    if (SPLIT) {  // below kSplitTokens * 16 units: 32-bit division
-      const int t = (int)u / nu;
-      const int c = ((int)u - t * nu) * UC;
-      combine_unit<K, Q8, UC>(a, t, c, min(c + UC, nch), lane);
-    } else {
-      combine_unit<K, Q8, kChunks>(a, u, 0, nch, lane);  // two groups of kChunks
-    }
+    // units <= 2^24 tokens x 16 chunks: 32-bit division
+    const int t = (int)u / nu;
+    const int c = ((int)u - t * nu) * UC;
+    combine_unit<K, Q8, UC>(a, t, c, min(c + UC, nch), lane);
   }
 }
 
@@ -174,26 +157,29 @@ __global__ __launch_bounds__(64 * WPB) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  // Small batches: chunk units, with 16-wave workgroups when the caller's
-  // cap leaves fewer 4-wave workgroups than chunk units need.
-  const bool split = a.T < kSplitTokens;
+  // One-chunk units.  Large batches run them on 16-wave workgroups (686-692
+  // against 708-712 us with 4, 8, 12 or 14 waves on a 30720-token batch);
+  // small ones on 4-wave workgroups so ~100 tokens reach every CU, or, when
+  // the caller's cap leaves fewer of those than units, on 16-wave
+  // workgroups of wide_chunks(K)-chunk units.
   const int nch = (a.H + 511) / 512;
-  const int64_t units = split ? a.T * (int64_t)nch : a.T;
-  const bool wide = split && (int64_t)a.max_blocks * kWavesPerBlock < units;
-  const int wpb = wide ? 16 : kWavesPerBlock;
+  const int64_t units = a.T * (int64_t)nch;
+  const bool big = a.T >= kWideTokens;
+  const bool wide = !big && (int64_t)a.max_blocks * kWavesPerBlock < units;
+  const int wpb = big || wide ? 16 : kWavesPerBlock;
   const int uc = wide_chunks(a.K);
   const int64_t wunits = wide ? a.T * (int64_t)((nch + uc - 1) / uc) : units;
   const int64_t need = (wunits + wpb - 1) / wpb;
   const unsigned grid = (unsigned)(need < a.max_blocks ? need : a.max_blocks);
   const bool q8 = a.fmt == MOEDC_FMT_Q8;
   switch (a.K) {
-#define MOEDC_LAUNCH(k, q)                                                     \
-  if (!split)                                                                  \
-    combine_kernel<k, q, false, kWavesPerBlock, 1><<<grid, 256, 0, s>>>(a);    \
-  else if (!wide)                                                              \
-    combine_kernel<k, q, true, kWavesPerBlock, 1><<<grid, 256, 0, s>>>(a);     \
-  else                                                                         \
-    combine_kernel<k, q, true, 16, wide_chunks(k)><<<grid, 1024, 0, s>>>(a);
+#define MOEDC_LAUNCH(k, q)                                                 \
+  if (big)                                                                 \
+    combine_kernel<k, q, 16, 1><<<grid, 1024, 0, s>>>(a);                  \
+  else if (!wide)                                                          \
+    combine_kernel<k, q, kWavesPerBlock, 1><<<grid, 256, 0, s>>>(a);       \
+  else                                                                     \
+    combine_kernel<k, q, 16, wide_chunks(k)><<<grid, 1024, 0, s>>>(a);
 #define MOEDC_CASE(k)          \
   case k:                      \
     if (q8) {                  \
