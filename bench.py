@@ -660,7 +660,7 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     # Kernels of the global workload's launches (whole-token combine, BF16);
     # the tags are name prefixes, so extra trailing template arguments match.
     missing = []
-    for key, tag in (("combine", "combine_kernel<8, false, false, 4"),
+    for key, tag in (("combine", "combine_kernel<8, false, 16, 1>"),
                      ("dispatch", "dispatch_token_block<false>"),
                      ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm<true>(")):
         kf = [k for k in fetch if tag in k]

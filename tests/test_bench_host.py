@@ -64,7 +64,7 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     tf = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, false, 4, 1>(moedc::CombineArgs)"
+    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, 16, 1>(moedc::CombineArgs)"
     _write_csv(str(tmp_path / "f" / "f_counter_collection.csv"), hdr,
                [[name, "FETCH_SIZE", 1000.0], [name, "FETCH_SIZE", 1000.0]])
     _write_csv(str(tmp_path / "w" / "w_counter_collection.csv"), hdr, [[name, "WRITE_SIZE", 500.0]])
