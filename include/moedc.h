@@ -210,8 +210,8 @@ moedc_status moedc_route_dispatch(const moedc_plan *plan, int32_t num_tokens,
 
 /*
  * moedc_combine on at most max_workgroups workgroups (each loops over the
- * batch; below 2048 tokens they run 16 waves each), leaving the other compute units to
- * concurrent work on other streams -- the pages' decode pipeline gives the
+ * batch with 16 waves when the cap binds), leaving the other compute units
+ * to concurrent work on other streams -- the pages' decode pipeline gives the
  * MoE path a fixed share of the cores ("Micro-batch Decode Pipeline" of the
  * CloudMatrix384 article).  Output identical to moedc_combine.
  * Errors: as moedc_combine; INVALID_ARG if max_workgroups < 1.
