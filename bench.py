@@ -275,7 +275,7 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 in/out, int8 payload + fp32 scales, fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
@@ -657,8 +657,10 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
                      f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
                      f"{copy_bytes}-byte copy); valid while source_sha matches."}
-    # Kernels of the global workload's launches (whole-token combine, BF16);
-    # the tags are name prefixes, so extra trailing template arguments match.
+    # Kernels of the global workload's launches: combine with one wave per
+    # 512-value chunk on 16-wave workgroups (BF16 input), dispatch with a
+    # workgroup per token; the tags are name prefixes, so extra trailing
+    # template arguments match.
     missing = []
     for key, tag in (("combine", "combine_kernel<8, false, 16, 1>"),
                      ("dispatch", "dispatch_token_block<false>"),

@@ -19,8 +19,10 @@
 // expert row in route order issues the loads of its chunks back to back.
 // Expert rows and the output are touched once, so loads and stores carry
 // the non-temporal hint.  A dropped entry (slot -1), like any slot outside
-// the plan's buffer, loads nothing and contributes fma(0, 0, acc) = acc
-// exactly.
+// the plan's buffer, loads nothing: its weight is 0 and its values are -0,
+// so it contributes fma(0, -0, acc) = 0 * -0 + acc = -0 + acc, which is acc
+// for every acc including both signed zeros (with +0 values an acc of -0,
+// left by a product that underflowed, would turn into +0).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -32,6 +34,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;  // below kWideTokens: spread over every CU
 constexpr int kWideTokens = 2048;   // from here on, 16-wave workgroups
+constexpr uint32_t kNegZero2 = 0x80008000u;  // two BF16 -0 values
 // Chunks per unit under a workgroup cap: 2 (twice the loads in flight per
 // wave), 1 from K = 14 on, where two chunks' loads no longer fit in the
 // 128 registers of a 16-wave workgroup.
@@ -89,7 +92,7 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           const int e = (g0 + c) * 512 + lane * 8;
-          v[c] = make_uint4(0, 0, 0, 0);
+          v[c] = make_uint4(kNegZero2, kNegZero2, kNegZero2, kNegZero2);
           if (slot[k] >= 0 && e < hend) v[c] = load_nt16(row + (int64_t)e * 2);
         }
 #pragma unroll
@@ -108,7 +111,7 @@ __device__ __forceinline__ void combine_unit(const CombineArgs &a, int64_t t, in
         for (int c = 0; c < CH; ++c) {
           const int e = (g0 + c) * 512 + lane * 8;
           v[c] = make_uint2(0, 0);
-          sc[c] = 0.0f;
+          sc[c] = -0.0f;  // (float)0 * -0 = -0
           if (slot[k] >= 0 && e < hend) {
             v[c] = load_nt8(row + e);
             sc[c] = *reinterpret_cast<const float *>(row + H + (a.per_token ? 0 : 4 * (e >> 7)));

@@ -131,12 +131,19 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
     w.capbase = o;       o = round_up(o + 4 * (int64_t)P, kWsAlign);
     w.rep_count = o;     o = round_up(o + 4 * (int64_t)E, kWsAlign);
     w.rep_table = o;     o = round_up(o + 4 * (int64_t)E * R, kWsAlign);
+    w.tables_end = o;
     w.block_counts = o;  o = round_up(o + 4 * (int64_t)p->nblk_max * P, kWsAlign);
     const int32_t ntiles = (c.hidden + kGemmChannels - 1) / kGemmChannels;
     p->gemm_nbe = (ntiles + kBandTiles - 1) / kBandTiles;
     p->gemm_J = (int32_t)(((int64_t)P * p->gemm_nbe + kXcds - 1) / kXcds);
     w.band_pre = o;      o = round_up(o + 4 * (int64_t)kXcds * (p->gemm_J + 1), kWsAlign);
     w.bytes = o;
+    p->table_image.assign((size_t)w.tables_end, 0);
+    const struct { int64_t off; const std::vector<int32_t> &v; } parts[] = {
+        {w.cap, p->cap}, {w.capbase, p->capbase}, {w.rep_count, p->rep_count},
+        {w.rep_table, p->rep_table}};
+    for (const auto &pt : parts)
+      std::memcpy(p->table_image.data() + pt.off, pt.v.data(), 4 * pt.v.size());
   } catch (...) {
     delete p;
     return MOEDC_ERR_NO_MEMORY;
@@ -163,20 +170,9 @@ moedc_status moedc_plan_sizes(const moedc_plan *p, moedc_sizes *out) {
 moedc_status moedc_plan_bind_workspace(const moedc_plan *p, void *ws, hipStream_t stream) {
   if (!p || !ws) return MOEDC_ERR_INVALID_ARG;
   if (!aligned16(ws)) return MOEDC_ERR_ALIGN;
-  const int32_t P = p->cfg.num_phys_experts, E = p->cfg.num_logical_experts;
-  const int32_t R = p->cfg.max_replicas;
-  struct Piece { int64_t off; const void *src; size_t bytes; } pieces[] = {
-      {p->ws.cap, p->cap.data(), 4 * (size_t)P},
-      {p->ws.capbase, p->capbase.data(), 4 * (size_t)P},
-      {p->ws.rep_count, p->rep_count.data(), 4 * (size_t)E},
-      {p->ws.rep_table, p->rep_table.data(), 4 * (size_t)E * R},
-  };
-  for (const Piece &pc : pieces) {
-    const hipError_t e = hipMemcpyAsync(ws_ptr<char>(ws, pc.off), pc.src, pc.bytes,
-                                        hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  return MOEDC_OK;
+  const hipError_t e = hipMemcpyAsync(ws, p->table_image.data(), p->table_image.size(),
+                                      hipMemcpyHostToDevice, stream);
+  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
 }
 
 }  // extern "C"
@@ -187,14 +183,11 @@ moedc_status check_route(const moedc_plan *p, int32_t T, const float *logits,
                          const int32_t *topk_ids, const float *topk_w, const int32_t *counts,
                          const int32_t *offsets, const int32_t *slots, const int32_t *dropped,
                          const void *ws) {
-  if (!p || !counts || !offsets || !dropped || !ws) return MOEDC_ERR_INVALID_ARG;
-  if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
-  if (T > 0 && (!logits || !topk_ids || !topk_w || !slots)) return MOEDC_ERR_INVALID_ARG;
-  if (!aligned16(ws) || !aligned4(counts) || !aligned4(offsets) || !aligned4(dropped))
-    return MOEDC_ERR_ALIGN;
-  if (T > 0 && (!aligned16(logits) || !aligned4(topk_ids) || !aligned4(topk_w) ||
-                !aligned4(slots)))
-    return MOEDC_ERR_ALIGN;
+  const moedc_status st = moedc::check_route_args(p, T, logits, topk_ids, topk_w, counts,
+                                                  offsets, slots, dropped);
+  if (st != MOEDC_OK) return st;
+  if (!ws) return MOEDC_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return MOEDC_ERR_ALIGN;
   return MOEDC_OK;
 }
 
@@ -211,6 +204,38 @@ moedc_status check_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,
 moedc::RouteArgs route_args(const moedc_plan *p, int32_t T, const float *logits,
                             int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets,
                             int32_t *slots, int32_t *dropped, void *ws) {
+  return moedc::route_args_at(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped,
+                              ws, ws_ptr<int32_t>(ws, p->ws.block_counts));
+}
+
+}  // namespace
+
+namespace moedc {
+
+moedc_status hip_status(hipError_t e) { return e == hipSuccess ? MOEDC_OK : hip_fail(e); }
+
+moedc_status check_route_args(const moedc_plan *p, int32_t T, const float *logits,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *dropped) {
+  if (!p || !counts || !offsets || !dropped) return MOEDC_ERR_INVALID_ARG;
+  if (T < 0 || T > p->cfg.max_tokens) return MOEDC_ERR_SHAPE;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !slots)) return MOEDC_ERR_INVALID_ARG;
+  if (!aligned4(counts) || !aligned4(offsets) || !aligned4(dropped)) return MOEDC_ERR_ALIGN;
+  if (T > 0 && (!aligned16(logits) || !aligned4(topk_ids) || !aligned4(topk_w) ||
+                !aligned4(slots)))
+    return MOEDC_ERR_ALIGN;
+  return MOEDC_OK;
+}
+
+hipError_t launch_route_any(const RouteArgs &a, hipStream_t s) {
+  return (a.T > 0 && a.T <= kFusedMaxTokens) ? launch_route_small(a, s) : launch_route(a, s);
+}
+
+RouteArgs route_args_at(const moedc_plan *p, int32_t T, const float *logits, int32_t *topk_ids,
+                        float *topk_w, int32_t *counts, int32_t *offsets, int32_t *slots,
+                        int32_t *dropped, const void *tables, int32_t *block_counts) {
+  void *ws = const_cast<void *>(tables);
   moedc::RouteArgs a{};
   a.logits = logits;
   a.topk_ids = topk_ids;
@@ -223,7 +248,7 @@ moedc::RouteArgs route_args(const moedc_plan *p, int32_t T, const float *logits,
   a.capbase = ws_ptr<const int32_t>(ws, p->ws.capbase);
   a.rep_count = ws_ptr<const int32_t>(ws, p->ws.rep_count);
   a.rep_table = ws_ptr<const int32_t>(ws, p->ws.rep_table);
-  a.block_counts = ws_ptr<int32_t>(ws, p->ws.block_counts);
+  a.block_counts = block_counts;
   a.T = T;
   a.E = p->cfg.num_logical_experts;
   a.P = p->cfg.num_phys_experts;
@@ -235,6 +260,10 @@ moedc::RouteArgs route_args(const moedc_plan *p, int32_t T, const float *logits,
   a.rep_identity = p->rep_identity;
   return a;
 }
+
+}  // namespace moedc
+
+namespace {
 
 moedc::DispatchArgs dispatch_args(const moedc_plan *p, int32_t T, const uint16_t *x,
                                   const int32_t *slots, void *dbuf) {
@@ -292,9 +321,7 @@ moedc_status moedc_route(const moedc_plan *p, int32_t T, const float *logits, in
   if (st != MOEDC_OK) return st;
   const moedc::RouteArgs ra =
       route_args(p, T, logits, topk_ids, topk_w, counts, offsets, slots, dropped, ws);
-  const hipError_t e = (T > 0 && T <= moedc::kFusedMaxTokens) ? moedc::launch_route_small(ra, stream)
-                                                               : moedc::launch_route(ra, stream);
-  return e == hipSuccess ? MOEDC_OK : hip_fail(e);
+  return moedc::hip_status(moedc::launch_route_any(ra, stream));
 }
 
 moedc_status moedc_dispatch(const moedc_plan *p, int32_t T, const uint16_t *x,

@@ -27,16 +27,22 @@ constexpr int kXcds = 8;
 constexpr int kBandTiles = 4;
 constexpr int kGemmChannels = 256;  // output channels per tile
 
-// Workspace byte offsets (all kWsAlign-aligned).
+// Workspace byte offsets (all kWsAlign-aligned).  The static tables come
+// first and form one contiguous image [0, tables_end) that the host keeps in
+// the plan and uploads with a single copy.
 struct WsLayout {
   int64_t cap = 0;          // int32 [P]
   int64_t capbase = 0;      // int32 [P]
   int64_t rep_count = 0;    // int32 [E]
   int64_t rep_table = 0;    // int32 [E][R]
+  int64_t tables_end = 0;   // end of the table image (<= kMaxTableBytes)
   int64_t block_counts = 0; // int32 [nblk_max][P]
   int64_t band_pre = 0;     // int32 [8][gemm_J+1]: expert GEMM work list per XCD
   int64_t bytes = 0;
 };
+// Largest table image: capacities and bases of 1024 physical experts, copy
+// counts and an 8-column replica table of 1024 logical experts.
+constexpr int64_t kMaxTableBytes = 4 * kMaxExperts * (3 + kMaxReplicas);
 
 struct RouteArgs {
   const float *logits;
@@ -74,7 +80,8 @@ struct CombineArgs {
   int32_t total_slots;  // entries outside [0, total_slots) are skipped
   int32_t T, H, K, fmt;
   int32_t per_token;    // Q8 input: one scale per token
-  int32_t max_blocks;   // grid cap (workgroups of 4 token waves); >= 1
+  int32_t max_blocks;   // grid cap in workgroups (4 waves, or 16 from 2048 tokens on and
+                        // whenever the cap binds); >= 1
 };
 
 struct StubArgs {
@@ -118,9 +125,33 @@ hipError_t launch_expert_gemm(const GemmArgs &a, int grid, hipStream_t s);
 
 }  // namespace moedc
 
+struct moedc_plan;
+
+namespace moedc {
+
+// Host helpers shared by the entry points (host.cpp).
+// Records e as the thread's last HIP error and returns MOEDC_ERR_HIP, or
+// MOEDC_OK for hipSuccess.
+moedc_status hip_status(hipError_t e);
+// Host-side argument checks of a route call, without the workspace.
+moedc_status check_route_args(const moedc_plan *p, int32_t T, const float *logits,
+                              const int32_t *topk_ids, const float *topk_w,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *slots, const int32_t *dropped);
+// Route kernel arguments with the plan's table image at `tables` (laid out as
+// in the workspace) and the per-block counts at `block_counts`.
+RouteArgs route_args_at(const moedc_plan *p, int32_t T, const float *logits, int32_t *topk_ids,
+                        float *topk_w, int32_t *counts, int32_t *offsets, int32_t *slots,
+                        int32_t *dropped, const void *tables, int32_t *block_counts);
+// Runs the route kernels for a small or large batch.
+hipError_t launch_route_any(const RouteArgs &a, hipStream_t s);
+
+}  // namespace moedc
+
 struct moedc_plan {
   moedc_config cfg;                 // pointer fields point into the vectors below
   std::vector<int32_t> cap, capbase, rep_count, rep_table;
+  std::vector<uint8_t> table_image;  // workspace bytes [0, ws.tables_end)
   int32_t K, G, nblk_max;
   int32_t rep_identity;             // no replicas and logical e == physical e
   int32_t gemm_nbe, gemm_J;         // expert GEMM bands per expert / per XCD

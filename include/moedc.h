@@ -121,7 +121,12 @@ moedc_status moedc_plan_bind_workspace(const moedc_plan *plan, void *workspace,
                                        hipStream_t stream);
 
 /*
- * Routing.  For each of num_tokens tokens:
+ * Routing: the routing metadata of "FusedDispatch and FusedCombine" in the
+ * CloudMatrix384 article (each token's experts, and where in each expert's
+ * pre-allocated receive buffer the token lands), over the expert placement
+ * of its "Decode Phase" (routed experts, redundant copies of popular
+ * experts, a shared expert every token visits).  For each of num_tokens
+ * tokens:
  *  - picks top_k logical experts by fp32 logit, highest first, ties to the
  *    lower id (-0 == +0), maps each to a physical copy, and computes its
  *    gate (score_fn); a shared expert, if configured, is appended last with

@@ -158,3 +158,28 @@ def sample_tokens(T, n, seed):
     rng = np.random.default_rng(seed)
     pick = rng.choice(T, size=n - 2, replace=False)
     return np.unique(np.concatenate([[0, T - 1], pick]))
+
+
+def assert_within_gate_bound(got, want, slots, gw, ow, rows_f64, chunk=512):
+    """End-to-end combine check when the device's gates feed its combine:
+    |got - want| <= 1 BF16 ulp + sum_k |dw_k| |y_k| + 2K u sum_k |w_k y_k|
+    per value, with want the oracle's combine on the oracle's gates ow, gw
+    the device's gates, and rows_f64(idx) the expert output rows at slot
+    indices idx ([n][K]) as float64 [n][K][H].  Every token is checked."""
+    T, K = slots.shape
+    gw = gw.astype(np.float64)
+    ow = ow.astype(np.float64)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        sl = slots[t0:t1]
+        keep = sl >= 0
+        yk = rows_f64(np.where(keep, sl, 0))
+        yk[~keep] = 0.0
+        a = bf16_to_f32(got[t0:t1]).astype(np.float64)
+        b = bf16_to_f32(want[t0:t1]).astype(np.float64)
+        mag = np.maximum(np.abs(a), np.abs(b))
+        ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
+        bound = ulp + (np.abs(gw[t0:t1] - ow[t0:t1])[:, :, None] * np.abs(yk)).sum(1) \
+            + 2 * K * U * (np.abs(ow[t0:t1])[:, :, None] * np.abs(yk)).sum(1)
+        bad = np.nonzero((np.abs(a - b) > bound).any(axis=1))[0]
+        assert bad.size == 0, f"token {t0 + bad[0]} outside the end-to-end bound"

@@ -17,7 +17,7 @@ import oracle
 from combine_moedc_route_amd import moedc as M
 from combine_moedc_route_amd import workloads as W
 
-from gpu_common import log
+from gpu_common import assert_within_gate_bound, bf16_to_f32, log
 
 pytestmark = pytest.mark.gpu
 
@@ -86,10 +86,12 @@ def test_decode_step_graph_replays_match_eager(fused):
 
 
 def test_large_batch_step_with_expert_layer_graph_replays_match_eager():
-    """The large-batch path in a graph: 3000 tokens (three route kernels,
-    whole-token dispatch and combine) and the W8A8 expert layer between
+    """The large-batch path in a graph: 3000 tokens (the large-batch route,
+    a workgroup per token in dispatch, one wave per 512-value chunk on
+    16-wave workgroups in combine) and the W8A8 expert layer between
     dispatch and combine, whose tile list is rebuilt on the device from
-    the route's counts on every replay."""
+    the route's counts on every replay.  The eager output is checked against
+    the oracle's expert layer and combine on every token."""
     # capacity 470 per expert against a mean of 450 entries: a few drops
     wl = dataclasses.replace(W.with_tokens(W.get("ragged"), 3000),
                              capacity=np.full(40, 470, np.int32))
@@ -119,6 +121,14 @@ def test_large_batch_step_with_expert_layer_graph_replays_match_eager():
     assert np.array_equal(ref["ids"].cpu().numpy(), want["topk_ids"])
     assert np.array_equal(ref["slots"].cpu().numpy(), want["slots"])
     assert int(ref["dropped"].item()) == want["dropped"] > 0
+    s = plan.sizes
+    dref = oracle.dispatch(cfg, x, want["slots"], s.total_slots, s.slot_stride)
+    eref = oracle.expert_w8a8(cfg, want["counts"], dref, s.slot_stride, Wt, wsc)
+    ywant = oracle.combine(cfg, eref, M.FMT_BF16, want["slots"], want["topk_w"])
+    assert_within_gate_bound(ref["y"].cpu().numpy().view(np.uint16), ywant, want["slots"],
+                             ref["w"].cpu().numpy(), want["topk_w"],
+                             lambda idx: bf16_to_f32(eref[idx]).astype(np.float64))
+    log("  eager step within the end-to-end bound of the oracle on every token")
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -12,10 +12,10 @@ import oracle
 from combine_moedc_route_amd import moedc as M
 from combine_moedc_route_amd import workloads as W
 
-from gpu_common import (SENTINEL, U, bf16_to_f32, check_dispatch_tokens,
+from gpu_common import (SENTINEL, U, assert_within_gate_bound, bf16_to_f32, check_dispatch_tokens,
                         check_dispatch_untouched, compare_route, dev, dev_i16,
                         expected_dispatch_buffer,
-                        gpu_dispatch, gpu_route, host_u16, log, sample_tokens,
+                        gpu_dispatch, gpu_route, host_u16, log,
                         ulp_diff_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -139,29 +139,7 @@ def test_dispatch_parity(name):
     log(f"  {n} slots bit-exact")
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_dispatch_parity_full_size(name):
-    wl, x, logits, plan, cfg = setup(name)
-    r = oracle.route(cfg, logits)
-    dbuf = gpu_dispatch(plan, x, r["slots"])
-    toks = sample_tokens(x.shape[0], 1024, 5)
-    n = check_dispatch_tokens(dbuf, x, r["slots"], toks, wl.hidden)
-    check_dispatch_untouched(dbuf, r["slots"], wl.hidden)
-    # Every kept copy of a token is byte-identical to its first copy.
-    H, G = wl.hidden, wl.hidden // 128
-    sl = torch.from_numpy(r["slots"].astype(np.int64)).cuda()
-    for t0 in range(0, x.shape[0], 4096):
-        blk = sl[t0:t0 + 4096]
-        first = dbuf[blk[:, 0], : H + 4 * G]
-        for k in range(1, wl.K):
-            keep = blk[:, k] >= 0
-            assert bool((dbuf[blk[keep, k], : H + 4 * G] == first[keep]).all())
-    # In every group with a nonzero scale some element is +-127.
-    q = dbuf[sl[:, 0], :H].view(torch.int8).view(-1, G, 128)
-    sc = dbuf[sl[:, 0], H:H + 4 * G].contiguous().view(torch.float32)
-    qmax = q.abs().amax(dim=2).to(torch.int32)
-    assert bool(((qmax == 127) | (sc == 0)).all())
-    log(f"  {n} sampled slots bit-exact; full-buffer properties hold")
+# Full-size batches (every token and slot): tests/test_gpu_full_size.py.
 
 
 # ------------------------------------------------------------------ combine
@@ -235,6 +213,56 @@ def test_combine_dropped_entries_and_signed_zero():
     got = host_u16(y)
     assert np.array_equal(got, want)
     assert (got[:3] == 0).all()
+
+
+@pytest.mark.parametrize("fmt", [M.FMT_BF16, M.FMT_Q8])
+@pytest.mark.parametrize("T,cap", [(300, None), (2500, None), (300, 2), (2500, 3)])
+def test_combine_skipped_entry_after_negative_zero(T, cap, fmt):
+    """A product that underflows to -0 leaves acc = -0; a later skipped entry
+    (slot -1 or outside the buffer) must leave it there (fmaf(w, y, +0) with
+    w * y in (-2^-150, 0) is -0, and the oracle skips the entry).  Rows:
+    entry 0 = the smallest negative subnormal times a gate that underflows it,
+    entry 1 skipped, entry 2 (some rows) a zero weight on a -0 value.  Small
+    and large batches, with and without a workgroup cap."""
+    K, H = 3, 640
+    wl = W.Workload("negzero", "", T, H, 4, 4, K, 0, W.SCORE_SIGMOID_NORM,
+                    np.full(4, T, np.int32), None, 0, "normal")
+    log(f"[case] negative zero T={T} cap={cap} fmt={fmt}")
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    s = plan.sizes
+    S = s.total_slots
+    rng = np.random.default_rng(98)
+    slots = np.stack([np.arange(T), np.full(T, -1), T + np.arange(T)], axis=1).astype(np.int32)
+    slots[1::3, 1] = S + 2                               # outside the buffer: skipped too
+    slots[2::5, 2] = -1
+    w = np.zeros((T, K), np.float32)
+    w[:, 0] = np.float32(1e-6)
+    w[::4, 0] = np.float32(0.5)                          # 0.5 * denorm_min: a tie, rounds to -0
+    w[:, 1] = rng.random(T, dtype=np.float32)
+    if fmt == M.FMT_BF16:
+        eout = W.make_expert_out_bf16(99, S, H)
+        eout[:T] = 0x8001                                # smallest negative BF16 subnormal
+        eout[T:2 * T] = 0x8000
+        src = dev_i16(eout)
+    else:
+        G = H // 128
+        eout = np.zeros((S, s.slot_stride), np.uint8)
+        eout[:, :H] = 0xFF                               # q = -1 everywhere
+        sc = np.full((S, G), np.float32(1.4e-45))        # the smallest subnormal scale
+        eout[:, H:H + 4 * G] = sc.view(np.uint8)
+        eout[T:2 * T, :H] = 0                            # q = 0 with scale -0: (float)0 * -0 = -0
+        eout[T:2 * T, H:H + 4 * G] = np.full((T, G), np.float32(-0.0)).view(np.uint8)
+        src = dev(eout)
+    clean = np.where((slots >= 0) & (slots < S), slots, -1).astype(np.int32)  # the oracle's view
+    want = oracle.combine(cfg, eout, fmt, clean, w)
+    assert (want[:, : H] == 0x8000).mean() > 0.5          # the case is exercised
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    if cap is None:
+        plan.combine(src, fmt, dev(slots), dev(w), y)
+    else:
+        plan.combine_limited(src, fmt, dev(slots), dev(w), y, cap)
+    assert np.array_equal(host_u16(y), want)
 
 
 @pytest.mark.parametrize("T", [300, 2500])     # chunk-unit and token-unit kernels
@@ -318,69 +346,6 @@ def test_bf16_rounding_every_upper_half_and_rounding_class():
     assert np.array_equal(got[:, ::128].ravel(), want[:, ::128].ravel())
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_combine_parity_full_size(name):
-    wl, x, logits, plan, cfg = setup(name)
-    r = oracle.route(cfg, logits)
-    s = plan.sizes
-    T, H, K = x.shape[0], wl.hidden, wl.K
-    cbuf = torch.zeros((s.total_slots, H), dtype=torch.int16, device="cuda")
-    toks = sample_tokens(T, 512, 6)
-    rows = r["slots"][toks]                      # [n][K]
-    kept = rows[rows >= 0]
-    vals = W.make_expert_out_bf16(17, kept.size, H)
-    cbuf[torch.from_numpy(kept.astype(np.int64)).cuda()] = dev_i16(vals)
-    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    plan.combine(cbuf, M.FMT_BF16, dev(r["slots"]), dev(r["topk_w"]), y)
-    got = host_u16(y[torch.from_numpy(toks).cuda()])
-    # Oracle on a compact buffer holding just the sampled tokens' rows.
-    compact = np.zeros((kept.size, H), np.uint16)
-    remap = np.full(rows.shape, -1, np.int32)
-    idx = 0
-    for i in range(rows.shape[0]):
-        for k in range(K):
-            if rows[i, k] >= 0:
-                compact[idx] = vals[idx]
-                remap[i, k] = idx
-                idx += 1
-    want = oracle.combine(cfg, compact, M.FMT_BF16, remap, r["topk_w"][toks])
-    assert ulp_diff_bf16(got, want).max(initial=0) <= 1
-    assert np.array_equal(got, want)
-    log(f"  {len(toks)} sampled tokens bit-exact")
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_combine_q8_full_size_sampled(name):
-    """Q8 combine over the GPU's own full-size dispatch; the oracle side
-    quantizes the sampled tokens itself into a compact slot buffer."""
-    wl, x, logits, plan, cfg = setup(name)
-    r = oracle.route(cfg, logits)
-    s = plan.sizes
-    T, H, K = x.shape[0], wl.hidden, wl.K
-    G = H // wl.group_size
-    dbuf = gpu_dispatch(plan, x, r["slots"])
-    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
-    plan.combine(dbuf, M.FMT_Q8, dev(r["slots"]), dev(r["topk_w"]), y)
-    toks = sample_tokens(T, 512, 8)
-    got = host_u16(y[torch.from_numpy(toks).cuda()])
-    del dbuf
-    q, sc = oracle.quantize_tokens(x[toks], wl.group_size)
-    rows = r["slots"][toks]
-    compact = np.zeros((int((rows >= 0).sum()), s.slot_stride), np.uint8)
-    remap = np.full(rows.shape, -1, np.int32)
-    idx = 0
-    for i in range(rows.shape[0]):
-        for k in range(K):
-            if rows[i, k] >= 0:
-                compact[idx, :H] = q[i].view(np.uint8)
-                compact[idx, H:H + 4 * G] = sc[i].view(np.uint8)
-                remap[i, k] = idx
-                idx += 1
-    want = oracle.combine(cfg, compact, M.FMT_Q8, remap, r["topk_w"][toks])
-    assert np.array_equal(got, want)
-    log(f"  {len(toks)} sampled tokens bit-exact (Q8)")
-
-
 def test_expert_layers_on_an_empty_batch_write_nothing():
     """All counts zero (the route of an empty batch): the expert layer's tile
     list is empty and neither it nor the stand-in writes anything."""
@@ -445,36 +410,24 @@ def _e2e(name):
     got_r["dropped"] = int(b["dropped"].item())
     compare_route(wl, got_r, r)
     s = plan.sizes
-    toks = sample_tokens(T, 256, 8)
     check_dispatch_tokens(b["dispatch_buf"].view(s.total_slots, s.slot_stride), x, r["slots"],
-                          toks, H, wl.group_size)
+                          np.arange(T), H, wl.group_size)
     # Final output: GPU gates differ from the oracle's by the gate tolerance,
     # so the bound is 1 BF16 ulp + sum_k |dw_k||y_k| + 2K u sum_k |w_k y_k|.
     dref = oracle.dispatch(cfg, x, r["slots"], s.total_slots, s.slot_stride)
     eref = dref if identity else oracle.expert_stub(cfg, r["counts"], dref, s.slot_stride)
     want = oracle.combine(cfg, eref, fmt, r["slots"], r["topk_w"])
-    got = host_u16(y)
-    gw = got_r["topk_w"].astype(np.float64)
-    ow = r["topk_w"].astype(np.float64)
-    for t in toks:
-        yk = np.zeros((K, H))
-        for k in range(K):
-            sl = r["slots"][t, k]
-            if sl < 0:
-                continue
-            if identity:
-                gs = wl.group_size
-                q = dref[sl, :H].view(np.int8).astype(np.float32)
-                sc = np.repeat(dref[sl, H:H + 4 * (H // gs)].view(np.float32), gs)
-                yk[k] = (q * sc).astype(np.float64)
-            else:
-                yk[k] = bf16_to_f32(eref[sl]).astype(np.float64)
-        a, bb = bf16_to_f32(got[t]).astype(np.float64), bf16_to_f32(want[t]).astype(np.float64)
-        mag = np.maximum(np.abs(a), np.abs(bb))
-        ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7), 2.0 ** -133)
-        bound = ulp + (np.abs(gw[t] - ow[t])[:, None] * np.abs(yk)).sum(0) \
-            + 2 * K * U * (np.abs(ow[t])[:, None] * np.abs(yk)).sum(0)
-        assert (np.abs(a - bb) <= bound).all(), t
+    gs = wl.group_size
+
+    def rows_f64(idx):
+        if identity:
+            q = dref[idx, :H].view(np.int8).astype(np.float32)             # [n][K][H]
+            sc = np.repeat(dref[idx, H:H + 4 * (H // gs)].view(np.float32), gs, axis=2)
+            return (q * sc).astype(np.float64)
+        return bf16_to_f32(eref[idx]).astype(np.float64)
+
+    assert_within_gate_bound(host_u16(y), want, r["slots"], got_r["topk_w"], r["topk_w"],
+                             rows_f64)
     return wl
 
 
@@ -547,7 +500,7 @@ def test_combine_limited_matches_combine(workgroups, fmt):
 
 
 @pytest.mark.parametrize("H,K", [(1152, 5), (640, 3), (1152, 15), (8192, 16), (128, 1), (4096, 13)])
-@pytest.mark.parametrize("T", [37, 300])
+@pytest.mark.parametrize("T", [37, 300, 2100, 3000])   # 2048+: 16-wave workgroups
 def test_combine_limited_unit_shapes(H, K, T):
     """Capped combine: multi-chunk units (a ragged last unit when the chunk
     count is odd), single-chunk units from K = 14, dropped entries; both
@@ -633,14 +586,19 @@ def test_expert_w8a8_full_size_sampled(group):
     plan.expert_w8a8(dev(r["counts"]), b["dispatch_buf"], Wd, wsd, b["combine_buf"],
                      b["workspace"])
     torch.cuda.synchronize()
-    dview = b["dispatch_buf"].view(s.total_slots, s.slot_stride)
     base = np.concatenate([[0], np.cumsum(wl.capacity)[:-1]])
+    owner = np.full(s.total_slots, -1, np.int64)          # slot -> token
+    kept = r["slots"] >= 0
+    owner[r["slots"][kept]] = np.nonzero(kept)[0]
     for p in (0, 77, 200, 255):
         n_p = min(int(r["counts"][p]), int(wl.capacity[p]))
         rows = np.unique(np.concatenate([[0, n_p - 1], np.arange(0, n_p, 97)]))
         sl = base[p] + rows
-        d = dview[torch.from_numpy(sl).cuda()].cpu().numpy()
+        # The sampled rows as the oracle's own dispatch writes them (one
+        # entry per token, slot i for the i-th sampled row).
         one = oracle.Cfg(H, 1, 1, 1, 0, 1, [len(rows)], group_size=wl.group_size)
+        d = oracle.dispatch(one, x[owner[sl]], np.arange(len(rows), dtype=np.int32)[:, None],
+                            len(rows), s.slot_stride)
         want = oracle.expert_w8a8(one, np.array([len(rows)], np.int32), d, s.slot_stride,
                                   Wd[p:p + 1].cpu().numpy(), wsd[p:p + 1].cpu().numpy())
         got = host_u16(b["combine_buf"][torch.from_numpy(sl).cuda()])
