@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoedc.so")
 SOURCES = ["route.hip", "dispatch.hip", "fused.hip", "combine.hip", "stub.hip",
-           "expert_gemm.hip", "host.cpp", "planning.cpp"]
+           "expert_gemm.hip", "noalloc.hip", "host.cpp", "planning.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

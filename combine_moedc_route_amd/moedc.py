@@ -27,6 +27,7 @@ EXPORTS = (
     "moedc_combine", "moedc_route_dispatch", "moedc_combine_limited",
     "moedc_expert_stub", "moedc_expert_w8a8", "moedc_place_replicas",
     "moedc_lpt_partition", "moedc_status_string", "moedc_last_hip_error",
+    "moedc_route_noalloc",
 )
 
 
@@ -117,6 +118,8 @@ def load_library(path):
     L.moedc_place_replicas.restype = i32
     L.moedc_lpt_partition.argtypes = [i32, P, P, i32, i32, i32, P, C.POINTER(C.c_double)]
     L.moedc_lpt_partition.restype = i32
+    L.moedc_route_noalloc.argtypes = [P, i32, P, P, P, P, P, P, P, P]
+    L.moedc_route_noalloc.restype = i32
     L.moedc_status_string.argtypes = [i32]
     L.moedc_status_string.restype = C.c_char_p
     L.moedc_last_hip_error.argtypes = []
@@ -286,6 +289,21 @@ class Plan:
         _check(lib().moedc_route(self._h, T, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
                                  _ptr(counts), _ptr(offsets), _ptr(slots), _ptr(dropped),
                                  _ptr(workspace), _stream(stream)), "moedc_route")
+
+    def route_noalloc(self, logits, topk_ids, topk_w, counts, offsets, slots, dropped,
+                      num_tokens: Optional[int] = None, stream=None):
+        """moedc_route on the library's static scratch array (no workspace)."""
+        T = logits.shape[0] if num_tokens is None else num_tokens
+        K, P = self.K, self.num_phys
+        _need(logits, "logits", T * self.num_logical, itemsize=4)
+        for t, what, n in ((topk_ids, "topk_ids", T * K), (topk_w, "topk_w", T * K),
+                           (counts, "counts", P), (offsets, "offsets", P + 1),
+                           (slots, "slots", T * K), (dropped, "dropped", 1)):
+            _need(t, what, n, itemsize=4)
+        _check(lib().moedc_route_noalloc(self._h, T, _ptr(logits), _ptr(topk_ids),
+                                         _ptr(topk_w), _ptr(counts), _ptr(offsets),
+                                         _ptr(slots), _ptr(dropped), _stream(stream)),
+               "moedc_route_noalloc")
 
     def dispatch(self, x, slots, dispatch_buf, num_tokens: Optional[int] = None,
                  stream=None):

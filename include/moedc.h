@@ -152,6 +152,30 @@ moedc_status moedc_route(const moedc_plan *plan, int32_t num_tokens,
                          int32_t *dropped, void *workspace, hipStream_t stream);
 
 /*
+ * moedc_route without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments (minus the workspace), outputs and
+ * errors as moedc_route, bit for bit the same results.  The per-block
+ * expert counts and the plan's tables live in a static device array of
+ * 16 MiB that the library holds on each GPU it runs on until the process
+ * ends; each call first copies the plan's tables (at most 44 KiB) into it
+ * with a host-to-device copy on `stream` -- the plan must stay alive until
+ * that copy has run -- and then runs the route kernels on it.  No device
+ * memory is allocated or freed.  Every call on a GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap on one
+ * GPU (other streams, other threads) race, and the caller must serialise
+ * them.  The stream must belong to the current device.
+ * Errors: as moedc_route; UNSUPPORTED when a batch needs more than the
+ * array holds, i.e. 4 * ceil(num_tokens / 64) * E_phys > 16 MiB - 64 KiB
+ * (e.g. more than 1,048,320 tokens at 256 physical experts); HIP when the
+ * array's address cannot be obtained or a copy or launch fails.
+ */
+moedc_status moedc_route_noalloc(const moedc_plan *plan, int32_t num_tokens,
+                                 const float *logits, int32_t *topk_ids, float *topk_w,
+                                 int32_t *counts, int32_t *offsets, int32_t *slots,
+                                 int32_t *dropped, hipStream_t stream);
+
+/*
  * Dispatch: early INT8 quantization with scales, then a direct
  * store of each token into each of its slots ("FusedDispatch and
  * FusedCombine": quantize before sending, write into pre-allocated

@@ -134,6 +134,13 @@ def test_call_validation_returns_before_launch():
     assert L.moedc_route_dispatch(h, 3, a16, a1, a16, a16, a16, a16, a16, a16, a16, a16,
                                   None) == M.ERR_ALIGN
     assert L.moedc_plan_bind_workspace(h, a1, None) == M.ERR_ALIGN
+    # the workspace-free route validates like moedc_route
+    assert L.moedc_route_noalloc(h, 65, a16, a16, a16, a16, a16, a16, a16, None) == M.ERR_SHAPE
+    assert L.moedc_route_noalloc(h, 4, None, a16, a16, a16, a16, a16, a16, None) == \
+        M.ERR_INVALID_ARG
+    assert L.moedc_route_noalloc(h, 4, a1, a16, a16, a16, a16, a16, a16, None) == M.ERR_ALIGN
+    assert L.moedc_route_noalloc(None, 4, a16, a16, a16, a16, a16, a16, a16, None) == \
+        M.ERR_INVALID_ARG
     assert L.moedc_plan_sizes(None, None) == M.ERR_INVALID_ARG
     out = C.c_void_p(123)
     assert L.moedc_plan_create(None, C.byref(out)) == M.ERR_INVALID_ARG and not out.value
@@ -196,3 +203,19 @@ def test_product_package_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "moedc_oracle" not in text, f
+
+
+def test_route_noalloc_refuses_batches_beyond_its_array():
+    """A batch whose per-block counts (4 B per 64 tokens and physical expert)
+    exceed the static array (16 MiB minus 64 KiB of tables) is refused with
+    UNSUPPORTED before any device call; the largest batch that fits is not."""
+    L = M.lib()
+    P = 1024
+    p = M.Plan(max_tokens=1 << 24, hidden=128, num_logical=P, num_phys=P, top_k=2,
+               capacity=np.full(P, 64, np.int32))
+    a16 = 0x10000
+    fits = ((16 << 20) - (64 << 10)) // (4 * P) * 64       # tokens whose counts just fit
+    st = L.moedc_route_noalloc(p._h, fits + 64, a16, a16, a16, a16, a16, a16, a16, None)
+    assert st == M.ERR_UNSUPPORTED
+    st = L.moedc_route_noalloc(p._h, 1 << 24, a16, a16, a16, a16, a16, a16, a16, None)
+    assert st == M.ERR_UNSUPPORTED
