@@ -18,9 +18,11 @@
 // tiles and ceil(H/256) channel tiles.  A band is kBandTiles channel tiles x all
 // row tiles of one expert (32 tiles for 8 row tiles), ordered row-major so
 // that neighbouring entries share a weight slice or a slot tile.  Bands are
-// dealt round-robin to the 8 XCDs; workgroup b runs on XCD b mod 8 (the
-// hardware's round-robin placement), and the 32 workgroups resident on one
-// XCD walk that XCD's band stream together.  The tiles of a band then run
+// dealt to the 8 XCDs by an LPT list schedule on their tile counts (or
+// round-robin, for comparison) on the device, from the route's counts;
+// workgroup b runs on XCD b mod 8 (the hardware's round-robin placement),
+// and the 32 workgroups resident on one XCD walk that XCD's band stream
+// together.  The tiles of a band then run
 // concurrently on one die, so each 256-channel weight slice and each slot
 // tile crosses from memory into that die's L2 about once per band instead
 // of once per tile.  The placement is only a performance assumption: any
@@ -62,35 +64,137 @@ constexpr int kThreads = 512;   // 8 waves: 2 token halves x 4 channel quarters
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// counts -> band_pre[x][j]: tiles in the bands x, x+8, ..., x+8(j-1) dealt
-// to XCD x (band k = expert k / nbe, channel tiles kBandTiles (k mod nbe) on);
-// band_pre[x][J] is XCD x's total.  J <= 1024 (P <= 1024, nbe <= 8).
+// counts -> each XCD's band list and tile prefix.  A band k (expert k / nbe,
+// channel tiles kBandTiles (k mod nbe) on) costs its tile count.
+//  - LPT (the longest-processing-time list schedule of "StrataCL 深度技术分析",
+//    section 3.5, with the 8 XCDs as the workers): bands with tiles, in
+//    order of cost descending (equal costs by index), each to the XCD with
+//    the fewest tiles so far (ties to the lower XCD).  Its largest XCD load
+//    is within 4/3 - 1/24 of the best possible.
+//  - Round-robin: band k to XCD k mod 8, in index order.
+// band_list[x][j] is XCD x's j-th band, band_pre[x][j] the tiles of its
+// bands before j, band_pre[x][band_cnt[x]] its total.  One workgroup; the
+// LPT pass sorts 32-bit keys (cost << 13 | 8191 - k, cost saturated at
+// 2^19 - 1) in LDS, then one wave places the bands in order.
+__device__ __forceinline__ int band_cost(const GemmArgs &a, int k) {
+  const int p = k / a.nbe, b = k - p * a.nbe;
+  const int rows = min(a.counts[p], a.cap[p]);
+  return (rows + a.bm - 1) / a.bm * min(kBandTiles, a.ntiles - b * kBandTiles);
+}
+
 __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
+  __shared__ uint32_t keys[kMaxBands];
   __shared__ int wsum[16];
-  const int j = threadIdx.x;
-  for (int x = 0; x < kXcds; ++x) {
-    const int k = x + kXcds * j;
-    int tiles = 0;
-    if (j < a.J && k < a.P * a.nbe) {
-      const int p = k / a.nbe, b = k % a.nbe;
-      const int rows = min(a.counts[p], a.cap[p]);
-      tiles = (rows + a.bm - 1) / a.bm * min(kBandTiles, a.ntiles - b * kBandTiles);
-    }
-    int incl = tiles;
+  const int tid = threadIdx.x;
+  const int nb = a.P * a.nbe;
+  const int Jm = a.Jmax;
+  if (a.dealing == MOEDC_DEAL_ROUND_ROBIN) {
+    for (int x = 0; x < kXcds; ++x) {
+      const int J = nb > x ? (nb - x + kXcds - 1) / kXcds : 0;
+      int32_t *pre = a.band_pre + x * (Jm + 1);
+      int carry = 0;
+      for (int j0 = 0; j0 < J; j0 += 1024) {
+        const int j = j0 + tid;
+        const int k = x + kXcds * j;
+        const int tiles = j < J ? band_cost(a, k) : 0;
+        if (j < J) a.band_list[x * Jm + j] = k;
+        int incl = tiles;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int u = __shfl_up(incl, d);
-      if ((j & 63) >= d) incl += u;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(incl, d);
+          if ((tid & 63) >= d) incl += u;
+        }
+        if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+        __syncthreads();
+        int base = carry;
+        for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+        if (j < J) pre[j] = base + incl - tiles;
+        int tot = 0;
+        for (int w = 0; w < 16; ++w) tot += wsum[w];
+        carry += tot;
+        __syncthreads();  // wsum is reused
+      }
+      if (tid == 0) {
+        pre[J] = carry;
+        a.band_cnt[x] = J;
+        if (a.xcd_tiles) a.xcd_tiles[x] = carry;
+      }
     }
-    if ((j & 63) == 63) wsum[j >> 6] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < (j >> 6); ++w) base += wsum[w];
-    int32_t *row = a.band_pre + x * (a.J + 1);
-    if (j < a.J) row[j] = base + incl - tiles;
-    if (j == a.J - 1) row[a.J] = base + incl;
-    __syncthreads();  // wsum is reused by the next XCD's scan
+    return;
   }
+  // ---- LPT ----
+  int n2 = 1;
+  while (n2 < nb) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) {
+    uint32_t key = 0u;
+    if (i < nb) key = ((uint32_t)min(band_cost(a, i), (1 << 19) - 1) << 13) | (uint32_t)(8191 - i);
+    keys[i] = key;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n2 >> 1); i += 1024) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint32_t x = keys[lo], y = keys[hi];
+        if ((x < y) == desc) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid >= 64) return;
+  // One wave, wave-uniform loop: loads and counts stay in scalar registers.
+  const int lane = tid;
+  int load[kXcds], cnt[kXcds];
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x) load[x] = cnt[x] = 0;
+  bool more = true;
+  for (int base = 0; base < nb && more; base += 64) {
+    // 64 bands at a time: each lane fetches one band's exact cost (the key
+    // holds a saturated one), then the wave places them one by one.
+    const uint32_t mine = base + lane < nb ? keys[base + lane] : 0u;
+    const int mine_k = 8191 - (int)(mine & 8191u);
+    const int mine_cost = (mine >> 13) ? band_cost(a, mine_k) : 0;
+    const int n = min(64, nb - base);
+    for (int i = 0; i < n; ++i) {
+      const int cost = __builtin_amdgcn_readlane(mine_cost, i);
+      if (cost == 0) {  // the rest have no tiles
+        more = false;
+        break;
+      }
+      const int k = __builtin_amdgcn_readlane(mine_k, i);
+      int bx = 0, bl = load[0];
+#pragma unroll
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < bl) {
+          bl = load[x];
+          bx = x;
+        }
+      int j = 0;
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) j = x == bx ? cnt[x] : j;
+      if (lane == 0) {
+        a.band_list[bx * Jm + j] = k;
+        a.band_pre[bx * (Jm + 1) + j] = bl;
+      }
+#pragma unroll
+      for (int x = 0; x < kXcds; ++x) {
+        load[x] += x == bx ? cost : 0;
+        cnt[x] += x == bx ? 1 : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x)
+    if (lane == x) {
+      a.band_pre[x * (Jm + 1) + cnt[x]] = load[x];
+      a.band_cnt[x] = cnt[x];
+      if (a.xcd_tiles) a.xcd_tiles[x] = load[x];
+    }
 }
 
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
@@ -166,17 +270,18 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
   const int spg = G128 ? 1 : a.steps_per_group;  // K steps per activation scale
   const int xcd = blockIdx.x % kXcds;
   const int nblk = gridDim.x / kXcds;  // workgroups sharing this XCD's stream
-  const int32_t *row = a.band_pre + xcd * (a.J + 1);
-  const int total = uniform(row[a.J]);
+  const int32_t *row = a.band_pre + xcd * (a.Jmax + 1);
+  const int J = uniform(a.band_cnt[xcd]);
+  const int total = uniform(row[J]);
 
   for (int q = blockIdx.x / kXcds; q < total; q += nblk) {
     // ---- locate the tile: band j of this XCD holds row[j] .. row[j+1) ----
-    int lo = 0, hi = a.J;
+    int lo = 0, hi = J;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (row[mid] <= q) lo = mid; else hi = mid;
     }
-    const int k = uniform(xcd + kXcds * lo);
+    const int k = uniform(a.band_list[xcd * a.Jmax + lo]);
     const int p = k / a.nbe, band = k % a.nbe;
     const int off = q - row[lo];
     const int w = min(kBandTiles, a.ntiles - band * kBandTiles);
@@ -342,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
 }  // namespace
 
 hipError_t launch_expert_gemm(const GemmArgs &args, int grid, hipStream_t s) {
-  if (args.J > 1024 || grid % kXcds) return hipErrorInvalidValue;
+  if (args.Jmax > kMaxBands || grid % kXcds) return hipErrorInvalidValue;
   GemmArgs a = args;
   a.bm = a.steps_per_group == 1 ? BM : BM_PT;  // the tile rows of the kernel below
   gemm_tiles<<<1, 1024, 0, s>>>(a);

@@ -135,8 +135,10 @@ moedc_status moedc_plan_create(const moedc_config *config, moedc_plan **out) {
     w.block_counts = o;  o = round_up(o + 4 * (int64_t)p->nblk_max * P, kWsAlign);
     const int32_t ntiles = (c.hidden + kGemmChannels - 1) / kGemmChannels;
     p->gemm_nbe = (ntiles + kBandTiles - 1) / kBandTiles;
-    p->gemm_J = (int32_t)(((int64_t)P * p->gemm_nbe + kXcds - 1) / kXcds);
-    w.band_pre = o;      o = round_up(o + 4 * (int64_t)kXcds * (p->gemm_J + 1), kWsAlign);
+    p->gemm_Jmax = P * p->gemm_nbe;
+    w.band_pre = o;      o = round_up(o + 4 * (int64_t)kXcds * (p->gemm_Jmax + 1), kWsAlign);
+    w.band_list = o;     o = round_up(o + 4 * (int64_t)kXcds * p->gemm_Jmax, kWsAlign);
+    w.band_cnt = o;      o = round_up(o + 4 * (int64_t)kXcds, kWsAlign);
     w.bytes = o;
     p->table_image.assign((size_t)w.tables_end, 0);
     const struct { int64_t off; const std::vector<int32_t> &v; } parts[] = {
@@ -368,9 +370,18 @@ moedc_status moedc_combine_limited(const moedc_plan *p, int32_t T, const void *e
 moedc_status moedc_expert_w8a8(const moedc_plan *p, const int32_t *counts, const void *dbuf,
                                const int8_t *weights, const float *w_scale,
                                uint16_t *ebuf, void *ws, hipStream_t stream) {
+  return moedc_expert_w8a8_dealt(p, counts, dbuf, weights, w_scale, ebuf, ws, MOEDC_DEAL_LPT,
+                                 nullptr, stream);
+}
+
+moedc_status moedc_expert_w8a8_dealt(const moedc_plan *p, const int32_t *counts, const void *dbuf,
+                                     const int8_t *weights, const float *w_scale, uint16_t *ebuf,
+                                     void *ws, int32_t dealing, int32_t *xcd_tiles,
+                                     hipStream_t stream) {
   if (!p || !counts || !dbuf || !weights || !w_scale || !ebuf || !ws) return MOEDC_ERR_INVALID_ARG;
+  if (dealing != MOEDC_DEAL_LPT && dealing != MOEDC_DEAL_ROUND_ROBIN) return MOEDC_ERR_INVALID_ARG;
   if (!aligned16(dbuf) || !aligned16(weights) || !aligned16(w_scale) || !aligned16(ebuf) ||
-      !aligned16(ws) || !aligned4(counts))
+      !aligned16(ws) || !aligned4(counts) || !aligned4(xcd_tiles))
     return MOEDC_ERR_ALIGN;
   moedc::GemmArgs a{};
   a.dbuf = static_cast<const uint8_t *>(dbuf);
@@ -381,13 +392,17 @@ moedc_status moedc_expert_w8a8(const moedc_plan *p, const int32_t *counts, const
   a.cap = ws_ptr<const int32_t>(ws, p->ws.cap);
   a.capbase = ws_ptr<const int32_t>(ws, p->ws.capbase);
   a.band_pre = ws_ptr<int32_t>(ws, p->ws.band_pre);
+  a.band_list = ws_ptr<int32_t>(ws, p->ws.band_list);
+  a.band_cnt = ws_ptr<int32_t>(ws, p->ws.band_cnt);
+  a.xcd_tiles = xcd_tiles;
+  a.dealing = dealing;
   a.slot_stride = p->slot_stride;
   a.H = p->cfg.hidden;
   a.P = p->cfg.num_phys_experts;
   a.ntiles = (p->cfg.hidden + moedc::kGemmChannels - 1) / moedc::kGemmChannels;
   a.steps_per_group = p->cfg.group_size / 128;
   a.nbe = p->gemm_nbe;
-  a.J = p->gemm_J;
+  a.Jmax = p->gemm_Jmax;
   // One persistent workgroup per CU: 32 on each of the 8 XCDs.
   const hipError_t e = moedc::launch_expert_gemm(a, 32 * moedc::kXcds, stream);
   return e == hipSuccess ? MOEDC_OK : hip_fail(e);

@@ -26,6 +26,7 @@ constexpr int64_t kWsAlign = 256;
 constexpr int kXcds = 8;
 constexpr int kBandTiles = 4;
 constexpr int kGemmChannels = 256;  // output channels per tile
+constexpr int kMaxBands = 8192;     // kMaxExperts x ceil(ceil(kMaxHidden / 256) / kBandTiles)
 
 // Workspace byte offsets (all kWsAlign-aligned).  The static tables come
 // first and form one contiguous image [0, tables_end) that the host keeps in
@@ -36,8 +37,10 @@ struct WsLayout {
   int64_t rep_count = 0;    // int32 [E]
   int64_t rep_table = 0;    // int32 [E][R]
   int64_t tables_end = 0;   // end of the table image (<= kMaxTableBytes)
-  int64_t block_counts = 0; // int32 [nblk_max][P]
-  int64_t band_pre = 0;     // int32 [8][gemm_J+1]: expert GEMM work list per XCD
+  int64_t block_counts = 0; // int32 [P][nblk_max]: the route's per-block expert counts
+  int64_t band_pre = 0;     // int32 [8][Jmax+1]: tile prefix of each XCD's bands (expert GEMM)
+  int64_t band_list = 0;    // int32 [8][Jmax]: each XCD's bands in order
+  int64_t band_cnt = 0;     // int32 [8]: bands per XCD
   int64_t bytes = 0;
 };
 // Largest table image: capacities and bases of 1024 physical experts, copy
@@ -56,7 +59,7 @@ struct RouteArgs {
   const int32_t *capbase;
   const int32_t *rep_count;
   const int32_t *rep_table;
-  int32_t *block_counts;
+  int32_t *block_counts;  // [P][ceil(T/64)]: per-block counts, then block prefixes
   int32_t T, E, P, R, K, KR, shared, score_fn;
   int32_t rep_identity;  // every logical expert e is physical expert e (one copy)
 };
@@ -105,11 +108,15 @@ struct GemmArgs {
   const int32_t *counts;
   const int32_t *cap;
   const int32_t *capbase;
-  int32_t *band_pre;        // [kXcds][J+1] exclusive tile prefix of each XCD's bands
+  int32_t *band_pre;        // [kXcds][Jmax+1] exclusive tile prefix of each XCD's bands
+  int32_t *band_list;       // [kXcds][Jmax] bands of each XCD, in the order walked
+  int32_t *band_cnt;        // [kXcds] bands per XCD
+  int32_t *xcd_tiles;       // device [kXcds] tiles per XCD, or null
   int64_t slot_stride;
   int32_t H, P, ntiles, steps_per_group;
   int32_t nbe;              // bands per expert: ceil(ntiles / kBandTiles)
-  int32_t J;                // bands per XCD: ceil(P * nbe / kXcds)
+  int32_t Jmax;             // bands in all: P * nbe (an XCD may get any number of them)
+  int32_t dealing;          // moedc_xcd_dealing
   int32_t bm;               // slot rows per tile (set by the launcher)
 };
 
@@ -154,7 +161,7 @@ struct moedc_plan {
   std::vector<uint8_t> table_image;  // workspace bytes [0, ws.tables_end)
   int32_t K, G, nblk_max;
   int32_t rep_identity;             // no replicas and logical e == physical e
-  int32_t gemm_nbe, gemm_J;         // expert GEMM bands per expert / per XCD
+  int32_t gemm_nbe, gemm_Jmax;      // expert GEMM bands per expert / in all
   int64_t slot_stride, combine_stride, total_slots;
   moedc::WsLayout ws;
 };

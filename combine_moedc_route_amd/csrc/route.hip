@@ -1,5 +1,5 @@
 // route.hip -- top-k routing, per-expert histogram, scans and slot
-// assignment on gfx950.
+// assignment for batches of more than 256 tokens (gfx950).
 //
 // What is computed follows the routing metadata of "CloudMatrix384:
 // Co-Designing Supernodes for Trillion-Parameter LLM Inference", sections
@@ -7,20 +7,41 @@
 // FusedCombine" (metadata that tells each sender where in the receiver's
 // pre-allocated buffer a token goes).  The slot of (token t, pick j) is the
 // expert's static base plus the rank of t among that expert's tokens in
-// ascending token order, so the layout is deterministic without atomics:
+// ascending token order, so the layout is deterministic without atomics.
 //
-//   K1 route_topk_rank  64 tokens x 4 lanes per block: top-k over LDS tiles
-//                       of the logits (next tile prefetched into registers),
-//                       4-way merge, gates, replica mapping; block-local
-//                       ranks and counts from per-expert 64-bit token masks
-//                       in LDS (popcounts); writes per-block expert counts.
-//   K2 route_block_scan one wave per expert: exclusive scan over blocks of
-//                       the per-block counts (DPP/shuffle wave scan); the
-//                       total is counts[p].
-//   K3 route_slots      one thread per entry: slot = base + block base +
-//                       in-block rank, or -1 past capacity; the last block
-//                       does the LDS-staged scan counts -> offsets and the
-//                       drop count.
+// K1 route_topk (a workgroup per 64 tokens, 4 lanes per token; lane `sub`
+//    holds columns 4 sub + 16 i + c, i < 16, c < 4, of each 256-column
+//    chunk of the logits, loaded as 16-byte vectors):
+//    - Top-k on packed keys.  A logit v of expert e becomes the 32-bit key
+//      (ok(v) with its low b bits replaced by 2^b - 1 - e), ok being the
+//      order-preserving integer image of the float and 2^b >= E: larger key
+//      = larger value, or the same high part and a lower id.  Each lane
+//      keeps its top KR + 1 keys sorted, one v_med3_u32 per list entry per
+//      logit (insertion is L[j] = med3(L[j-1], L[j], c), L[0] = max(L[0],
+//      c)), and the token's four lists merge through quad DPP.
+//    - Exactness.  Where the high parts (the key without the id bits) of
+//      the merged top KR + 1 strictly decrease, the first KR keys are the
+//      top KR logits by (value desc, id asc) in that order: every other
+//      logit has a smaller high part than the KR-th, hence a smaller value.
+//      Two cases need more.  If the KR-th and the (KR+1)-th key share their
+//      high part h, the logits with high part h (the boundary class) are
+//      ranked again on their own, by a second med3 pass keyed on the low b
+//      bits of ok (the part the packed key dropped) and the id -- exact,
+//      since the class shares h -- and fill the positions below the picks
+//      with higher high parts.  If only picks share a high part, their set
+//      is right and only their order needs the exact values, which are
+//      re-read for the gates anyway: the token's picks are then sorted by
+//      (ok desc, id asc).
+//    - Gates, replica mapping, outputs; the token's bit in a per-expert
+//      64-bit mask in LDS (atomic OR, order free).  The block-local rank of
+//      an entry, the popcount of the lower bits of its expert's mask, goes
+//      into slots; the block's count of each expert into block_counts[p][b]
+//      (expert-major, so K2 reads one contiguous row per expert).
+// K2 route_scan: a wave per expert: exclusive scan of its row of block
+//    counts (in place) and the expert's total, counts[p].
+// K3 route_slots: a thread per entry: slot = base + block prefix +
+//    block-local rank, or -1 past capacity; the last workgroup scans counts
+//    into offsets through LDS and sums the drops.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -30,240 +51,353 @@ namespace moedc {
 
 namespace {
 
-constexpr int kSub = 4;                    // lanes per token in the top-k scan
-constexpr int kTileE = 64;                 // experts per LDS tile (16 per lane)
-static_assert(kRouteTokens * kSub == 256, "one token per lane of wave 0");
+constexpr int kSub = 4;           // lanes per token
+constexpr int kLaneCols = 64;     // columns per lane per chunk (256 per token)
+constexpr int kChunkCols = kSub * kLaneCols;
+static_assert(kRouteTokens * kSub == 256, "64 tokens x 4 lanes per workgroup");
 
-// Insert (v, e) into a list kept in descending value order; equal values
-// keep the earlier (lower-id) entry first because ids arrive ascending.
-// Branch-free (selects only): slot j takes the new entry, or slot j-1's old
-// one when the new entry lands above it; slots are updated from the bottom
-// up, so slot j-1 is still unmodified when slot j reads it.
-template <int KR>
-__device__ __forceinline__ void topk_insert(float (&val)[KR], int (&id)[KR], float v, int e) {
-#pragma unroll
-  for (int j = KR - 1; j > 0; --j) {
-    const bool take = v > val[j];
-    const bool shift = v > val[j - 1];  // the new value lands above slot j
-    const float nv = shift ? val[j - 1] : v;
-    const int ni = shift ? id[j - 1] : e;
-    val[j] = take ? nv : val[j];
-    id[j] = take ? ni : id[j];
-  }
-  const bool take0 = v > val[0];
-  val[0] = take0 ? v : val[0];
-  id[0] = take0 ? e : id[0];
+// Order-preserving integer image of a float; -0 and +0 map to one key.
+__device__ __forceinline__ uint32_t okey(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float okey_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// A thread's share of one 64-expert tile of the block's logits, held in
-// registers so the next tile's loads are in flight while this one is scanned.
-struct TileRegs {
-  float v[kRouteTokens * kTileE / 256];
-};
+// v_med3_u32, written as an instruction: the same median spelled as nested
+// min/max makes LLVM's n-ary reassociation pass run for minutes on the long
+// insertion chains below.
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
-__device__ __forceinline__ void tile_fetch(TileRegs &tr, const RouteArgs &a, int64_t row0,
-                                           int e0, int ec, bool vec4) {
-  const int tid = threadIdx.x;
-  if (vec4) {  // E % 4 == 0: rows are 16-byte aligned and ec is a multiple of 4
+// Insert c into a descending list (the smallest entry falls off).
+template <int N>
+__device__ __forceinline__ void list_insert(uint32_t (&L)[N], uint32_t c) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row0 + r < a.T && c < ec)
-        x = *reinterpret_cast<const float4 *>(a.logits + (row0 + r) * a.E + e0 + c);
-      tr.v[4 * j] = x.x;
-      tr.v[4 * j + 1] = x.y;
-      tr.v[4 * j + 2] = x.z;
-      tr.v[4 * j + 3] = x.w;
+  for (int j = N - 1; j > 0; --j) L[j] = med3u(L[j - 1], L[j], c);
+  L[0] = max(L[0], c);
+}
+
+// L := the top N of L and the list of the quad lane selected by CTRL.  The
+// partner's entries arrive in descending order, so entry j can only land
+// at position j or below: its insertion skips the positions above.
+template <int N, int CTRL>
+__device__ __forceinline__ void list_merge(uint32_t (&L)[N]) {
+  uint32_t o[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) o[j] = dpp<CTRL>(L[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+#pragma unroll
+    for (int i = N - 1; i > j; --i) L[i] = med3u(L[i - 1], L[i], o[j]);
+    L[j] = max(L[j], o[j]);
+  }
+}
+
+// quad_perm control that broadcasts quad lane q to all four lanes.
+__host__ __device__ constexpr int quad_bcast(int q) { return q | (q << 2) | (q << 4) | (q << 6); }
+
+__device__ __forceinline__ uint32_t quad_get(uint32_t v, int q) {
+  switch (q) {
+    case 0: return dpp<quad_bcast(0)>(v);
+    case 1: return dpp<quad_bcast(1)>(v);
+    case 2: return dpp<quad_bcast(2)>(v);
+    default: return dpp<quad_bcast(3)>(v);
+  }
+}
+
+// Lane `sub` of token t loads its 64 columns of chunk c0 (columns past E and
+// tokens past T read as -inf).
+__device__ __forceinline__ void load_chunk(float (&v)[kLaneCols], const RouteArgs &a, int64_t t,
+                                           bool active, int c0, int sub, bool vec4) {
+  const float *row = a.logits + t * a.E + c0;
+  const int left = a.E - c0;
+  if (vec4) {  // E % 4 == 0: 16-byte aligned rows, and left is a multiple of 4
+#pragma unroll
+    for (int i = 0; i < kLaneCols / 4; ++i) {
+      const int c = 4 * sub + 16 * i;
+      float4 x = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(),
+                             -__builtin_inff());
+      if (active && c < left) x = *reinterpret_cast<const float4 *>(row + c);
+      v[4 * i] = x.x;
+      v[4 * i + 1] = x.y;
+      v[4 * i + 2] = x.z;
+      v[4 * i + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int f = tid + 256 * j, r = f / kTileE, c = f % kTileE;
-      tr.v[j] = (row0 + r < a.T && c < ec) ? a.logits[(row0 + r) * a.E + e0 + c] : 0.f;
+    for (int i = 0; i < kLaneCols; ++i) {
+      const int c = 4 * sub + 16 * (i >> 2) + (i & 3);
+      v[i] = (active && c < left) ? row[c] : -__builtin_inff();
     }
   }
 }
 
-__device__ __forceinline__ void tile_store(float (&tile)[kRouteTokens][kTileE + 1],
-                                           const TileRegs &tr, bool vec4) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ int lane_col(int c0, int sub, int i) {
+  return c0 + 4 * sub + 16 * (i >> 2) + (i & 3);
+}
+
+// Group g (of 4) of a lane's chunk, columns lane_col(c0, sub, 16 g + u),
+// u < 16, for the rare passes over rows of more than 256 logits (read again
+// from memory, L2-resident by then).  Reading group by group in a loop that
+// is not unrolled keeps those passes short without indexing a register
+// array by a loop counter.
+__device__ __forceinline__ void load_group(float (&w)[16], const RouteArgs &a, int64_t t, int c0,
+                                           int g, int sub, bool vec4) {
+  const float *row = a.logits + t * a.E + c0;
+  const int left = a.E - c0;
   if (vec4) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int f = tid + 256 * j, r = f / (kTileE / 4), c = (f % (kTileE / 4)) * 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tile[r][c + i] = tr.v[4 * j + i];
+    for (int u = 0; u < 4; ++u) {
+      const int c = 4 * sub + 16 * (4 * g + u);
+      float4 x = make_float4(-__builtin_inff(), -__builtin_inff(), -__builtin_inff(),
+                             -__builtin_inff());
+      if (c < left) x = *reinterpret_cast<const float4 *>(row + c);
+      w[4 * u] = x.x;
+      w[4 * u + 1] = x.y;
+      w[4 * u + 2] = x.z;
+      w[4 * u + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int f = tid + 256 * j;
-      tile[f / kTileE][f % kTileE] = tr.v[j];
+    for (int u = 0; u < 16; ++u) {
+      const int c = 4 * sub + 16 * (4 * g + (u >> 2)) + (u & 3);
+      w[u] = c < left ? row[c] : -__builtin_inff();
     }
   }
 }
 
-// One block = kRouteTokens tokens x kSub lanes.  Lane `sub` of token r scans
-// columns [16 sub, 16 sub + 16) of every 64-expert tile and keeps a local
-// top-KR; wave 0 (lane = token) merges the four lists, computes gates and the
-// physical ids.  Ranks come from one 64-bit token mask per expert in LDS:
-// bit l of mask[p] is set iff token l of the block routes to p (atomic OR,
-// so the result does not depend on arrival order); a token's rank for p is
-// the popcount of the mask below its bit, the block's count the full
-// popcount.
+// Boundary-class key: logits whose high part is h, ranked by the low bits
+// of ok and then the id; everything else 0.
+__device__ __forceinline__ uint32_t class_key(float x, int e, int E, uint32_t h, int idbits,
+                                              uint32_t idmask) {
+  const uint32_t k = okey(x);
+  return (e < E && (k >> idbits) == h) ? (((k & idmask) << idbits) | (idmask - (uint32_t)e)) : 0u;
+}
+
 template <int KR, bool SHARED>
-__global__ __launch_bounds__(256) void route_topk_rank(RouteArgs a) {
+__global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int nblk) {
   constexpr int KT = KR + (SHARED ? 1 : 0);
-  __shared__ float tile[kRouteTokens][kTileE + 1];
-  // Token-minor, so the merge's reads (lane = token, each at its own list
-  // position) hit distinct banks.
-  __shared__ float lval[kSub][KR][kRouteTokens];
-  __shared__ int lid[kSub][KR][kRouteTokens];
-  __shared__ float zpart[kRouteTokens][kSub];
-  __shared__ float mrow[kRouteTokens];
+  constexpr int N = KR + 1;                   // one key past the picks, for the exactness test
+  constexpr int NP = (KT + kSub - 1) / kSub;  // picks per lane
   __shared__ unsigned long long tokmask[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int r = tid >> 2, sub = tid & 3;
-  const int64_t row0 = (int64_t)blockIdx.x * kRouteTokens;
   const int E = a.E, P = a.P;
-  const bool vec4 = (E & 3) == 0;
-
+  const int blk = blockIdx.x;
   for (int i = tid; i < P; i += 256) tokmask[i] = 0ull;
 
-  // ---- scan: local top-KR over this lane's columns ----------------------
-  float val[KR];
-  int id[KR];
+  const int64_t t = (int64_t)blk * kRouteTokens + r;
+  const bool active = t < a.T;
+  const bool vec4 = (E & 3) == 0;
+  const uint32_t idmask = (1u << idbits) - 1u;
+
+  // ---- packed-key top-(KR+1) per lane, merged over the token's quad -------
+  uint32_t L[N];
 #pragma unroll
-  for (int j = 0; j < KR; ++j) {
-    val[j] = -__builtin_inff();
-    id[j] = j;  // valid ids even if a row has no finite logit
-  }
-  TileRegs tr;
-  tile_fetch(tr, a, row0, 0, min(kTileE, E), vec4);
-  for (int e0 = 0; e0 < E; e0 += kTileE) {
-    const int ec = min(kTileE, E - e0);
-    __syncthreads();
-    tile_store(tile, tr, vec4);
-    __syncthreads();
-    if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
-    if (ec == kTileE) {  // full tile (block-uniform): a fixed, unrolled scan
+  for (int j = 0; j < N; ++j) L[j] = 0u;  // below every real key
+  float v[kLaneCols];
+  for (int c0 = 0; c0 < E; c0 += kChunkCols) {
+    load_chunk(v, a, t, active, c0, sub, vec4);
 #pragma unroll
-      for (int i = 0; i < kTileE / kSub; ++i)
-        topk_insert<KR>(val, id, tile[r][16 * sub + i], e0 + 16 * sub + i);
-    } else {
-      const int c1 = min(16 * sub + 16, ec);
-      for (int c = 16 * sub; c < c1; ++c) topk_insert<KR>(val, id, tile[r][c], e0 + c);
+    for (int i = 0; i < kLaneCols; ++i) {
+      const int e = lane_col(c0, sub, i);
+      const uint32_t key = (okey(v[i]) & ~idmask) | (idmask - (uint32_t)e);
+      list_insert<N>(L, e < E ? key : 0u);
     }
   }
-#pragma unroll
-  for (int j = 0; j < KR; ++j) {
-    lval[sub][j][r] = val[j];
-    lid[sub][j][r] = id[j];
-  }
-  __syncthreads();
+  list_merge<N, kDppQuadXor1>(L);
+  list_merge<N, kDppQuadXor2>(L);
 
-  // ---- wave 0: merge the four lists (value desc, id asc) -----------------
-  const int64_t t = row0 + tid;
-  const bool active = tid < kRouteTokens && t < a.T;
-  if (tid < kRouteTokens) {
-    int h[kSub] = {0, 0, 0, 0};  // next unread entry of each lane's list
+  int id[KR];
 #pragma unroll
-    for (int j = 0; j < KR; ++j) {
-      float bv = -__builtin_inff();
-      int bi = 0, bs = -1;
+  for (int j = 0; j < KR; ++j) id[j] = (int)(idmask - (L[j] & idmask));
+  bool inner = false;
 #pragma unroll
-      for (int s2 = 0; s2 < kSub; ++s2) {
-        if (h[s2] < KR) {
-          const float v = lval[s2][h[s2]][tid];
-          const int i = lid[s2][h[s2]][tid];
-          if (bs < 0 || v > bv || (v == bv && i < bi)) {
-            bv = v;
-            bi = i;
-            bs = s2;
+  for (int j = 0; j + 1 < KR; ++j) inner |= (L[j] >> idbits) == (L[j + 1] >> idbits);
+  const uint32_t hmin = L[KR - 1] >> idbits;
+  const bool bnd = active && hmin == (L[KR] >> idbits);
+  inner = inner && active;
+
+  // ---- boundary class: rank the logits of high part hmin by their low bits
+  // (whole quads take this together: the merged list is the quad's).
+  if (__builtin_amdgcn_ballot_w64(bnd)) {
+    if (bnd) {
+      int above = 0;  // picks with a higher high part keep their places
+#pragma unroll
+      for (int j = 0; j < KR; ++j) above += (L[j] >> idbits) > hmin;
+      uint32_t C[KR];
+#pragma unroll
+      for (int j = 0; j < KR; ++j) C[j] = 0u;
+      if (E <= kChunkCols) {  // the row is still in registers
+#pragma unroll
+        for (int i = 0; i < kLaneCols; ++i)
+          list_insert<KR>(C, class_key(v[i], lane_col(0, sub, i), E, hmin, idbits, idmask));
+      } else {
+        for (int c0 = 0; c0 < E; c0 += kChunkCols) {
+#pragma unroll 1
+          for (int g = 0; g < kLaneCols / 16; ++g) {
+            float w[16];
+            load_group(w, a, t, c0, g, sub, vec4);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              list_insert<KR>(C, class_key(w[u], lane_col(c0, sub, 16 * g + u), E, hmin, idbits,
+                                           idmask));
           }
         }
       }
-      val[j] = bv;
-      id[j] = bi;
-#pragma unroll
-      for (int s2 = 0; s2 < kSub; ++s2) h[s2] += bs == s2;
-    }
-    mrow[tid] = val[0];
-  }
-
-  // ---- softmax denominator: second pass over the tiles ---------------------
-  float Z = 0.0f;
-  if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
-    __syncthreads();
-    const float m = mrow[r];
-    float z = 0.0f;
-    tile_fetch(tr, a, row0, 0, min(kTileE, E), vec4);
-    for (int e0 = 0; e0 < E; e0 += kTileE) {
-      const int ec = min(kTileE, E - e0);
-      __syncthreads();
-      tile_store(tile, tr, vec4);
-      __syncthreads();
-      if (e0 + kTileE < E) tile_fetch(tr, a, row0, e0 + kTileE, min(kTileE, E - e0 - kTileE), vec4);
-      if (ec == kTileE) {
-#pragma unroll
-        for (int i = 0; i < kTileE / kSub; ++i) z += expf(tile[r][16 * sub + i] - m);
-      } else {
-        const int c1 = min(16 * sub + 16, ec);
-        for (int c = 16 * sub; c < c1; ++c) z += expf(tile[r][c] - m);
-      }
-    }
-    zpart[r][sub] = z;
-    __syncthreads();
-    if (tid < kRouteTokens) Z = ((zpart[tid][0] + zpart[tid][1]) + zpart[tid][2]) + zpart[tid][3];
-  }
-
-  // ---- wave 0: gates, physical ids, outputs, token masks --------------------
-  int pk[KT];
-  if (tid < kRouteTokens) {
-    float w[KT];
-    if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
-#pragma unroll
-      for (int j = 0; j < KR; ++j) w[j] = expf(val[j] - val[0]) / Z;
-    } else {
-      float sg[KR];
-      float S = 0.0f;
+      list_merge<KR, kDppQuadXor1>(C);
+      list_merge<KR, kDppQuadXor2>(C);
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
-        sg[j] = 1.0f / (1.0f + expf(-val[j]));
-        S += sg[j];
+        // position j takes class entry j - above (compile-time j, runtime above)
+        uint32_t c = 0u;
+#pragma unroll
+        for (int q = 0; q <= j; ++q) c = (j - q == above) ? C[q] : c;
+        // The class holds at least KR - above + 1 logits (positions above..KR
+        // of the merged list), so c is a real key; the test keeps ids in range
+        // regardless.
+        if (j >= above && c != 0u) id[j] = (int)(idmask - (c & idmask));
+      }
+    }
+  }
+
+  // ---- exact logits of this lane's picks (j = sub + 4 i) ---------------------
+  int pid[NP];
+  float pv[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int j = sub + kSub * i;
+    int e = 0;
+#pragma unroll
+    for (int q = 0; q < kSub; ++q)
+      if (kSub * i + q < KR) e = (sub == q) ? id[kSub * i + q] : e;
+    pid[i] = e;
+    pv[i] = (active && j < KR) ? a.logits[t * E + e] : 0.0f;
+  }
+  // Picks that share a high part: order them by (value desc, id asc).
+  if (__builtin_amdgcn_ballot_w64(inner || bnd)) {
+    if (inner || bnd) {
+      uint32_t sk[KR];
+      int si[KR];
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        sk[j] = 0u;
+        si[j] = 0x7FFFFFFF;
       }
 #pragma unroll
-      for (int j = 0; j < KR; ++j) w[j] = sg[j] / S;
-    }
+      for (int j = 0; j < KR; ++j) {  // gather pick j from quad lane j % 4, then insert
+        const uint32_t k = quad_get(okey(pv[j / kSub]), j % kSub);
+        const int e = (int)quad_get((uint32_t)pid[j / kSub], j % kSub);
 #pragma unroll
-    for (int j = 0; j < KR; ++j) {  // replica copy t mod r_e
-      const int e = id[j];
-      pk[j] = a.rep_identity ? e : a.rep_table[e * a.R + (int)t % a.rep_count[e]];
+        for (int s = KR - 1; s > 0; --s) {  // exact insertion, bottom up
+          const bool take = k > sk[s] || (k == sk[s] && e < si[s]);
+          const bool shift = k > sk[s - 1] || (k == sk[s - 1] && e < si[s - 1]);
+          const uint32_t nk = shift ? sk[s - 1] : k;
+          const int ni = shift ? si[s - 1] : e;
+          sk[s] = take ? nk : sk[s];
+          si[s] = take ? ni : si[s];
+        }
+        const bool take0 = k > sk[0] || (k == sk[0] && e < si[0]);
+        sk[0] = take0 ? k : sk[0];
+        si[0] = take0 ? e : si[0];
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        uint32_t k = 0u;
+        int e = 0;
+#pragma unroll
+        for (int q = 0; q < kSub; ++q)
+          if (kSub * i + q < KR && sub == q) {
+            k = sk[kSub * i + q];
+            e = si[kSub * i + q];
+          }
+        if (sub + kSub * i < KR) {
+          pid[i] = e;
+          pv[i] = okey_float(k);
+        }
+      }
     }
-    if (SHARED) {
-      pk[KT - 1] = P - 1;
-      w[KT - 1] = 1.0f;
-    }
+  }
+
+  // ---- gates, physical ids, outputs, token masks ------------------------------
+  float w[NP];
+  if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
+    // Z = sum over all logits of exp(l - max), per lane in column order,
+    // then lanes 0..3 in order.
+    const float m = __uint_as_float(dpp<quad_bcast(0)>(__float_as_uint(pv[0])));
+    float z = 0.0f;
     if (active) {
+      if (E <= kChunkCols) {
 #pragma unroll
-      for (int j = 0; j < KT; ++j) {
-        a.topk_ids[t * KT + j] = pk[j];
-        a.topk_w[t * KT + j] = w[j];
-        atomicOr(&tokmask[pk[j]], 1ull << tid);
+        for (int i = 0; i < kLaneCols; ++i)
+          if (lane_col(0, sub, i) < E) z += expf(v[i] - m);
+      } else {
+        for (int c0 = 0; c0 < E; c0 += kChunkCols) {
+#pragma unroll 1
+          for (int g = 0; g < kLaneCols / 16; ++g) {
+            float x[16];
+            load_group(x, a, t, c0, g, sub, vec4);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              if (lane_col(c0, sub, 16 * g + u) < E) z += expf(x[u] - m);
+          }
+        }
       }
+    }
+    const float Z = ((__uint_as_float(quad_get(__float_as_uint(z), 0)) +
+                      __uint_as_float(quad_get(__float_as_uint(z), 1))) +
+                     __uint_as_float(quad_get(__float_as_uint(z), 2))) +
+                    __uint_as_float(quad_get(__float_as_uint(z), 3));
+#pragma unroll
+    for (int i = 0; i < NP; ++i) w[i] = expf(pv[i] - m) / Z;
+  } else {
+    // Sigmoid of each pick, normalised by their sum taken in pick order.
+    float s[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) s[i] = 1.0f / (1.0f + expf(-pv[i]));
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KR; ++j)
+      S += __uint_as_float(quad_get(__float_as_uint(s[j / kSub]), j % kSub));
+#pragma unroll
+    for (int i = 0; i < NP; ++i) w[i] = s[i] / S;
+  }
+  int pk[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int j = sub + kSub * i;
+    const int e = pid[i];
+    pk[i] = -1;
+    // (tokens past T hold padding ids: no table lookup for them)
+    if (active && j < KR)
+      pk[i] = a.rep_identity ? e : a.rep_table[e * a.R + (int)(t % a.rep_count[e])];
+    if (SHARED && j == KT - 1) {
+      pk[i] = P - 1;
+      w[i] = 1.0f;
+    }
+    if (active && j < KT) {
+      a.topk_ids[t * KT + j] = pk[i];
+      a.topk_w[t * KT + j] = w[i];
+      atomicOr(&tokmask[pk[i]], 1ull << r);
     }
   }
   __syncthreads();
-  if (active) {
-    const uint64_t lt = lanemask_lt();
+
+  // ---- block-local ranks (finished by route_slots) and block counts ----------
+  const uint64_t below = r == 0 ? 0ull : (~0ull >> (64 - r));
 #pragma unroll
-    for (int j = 0; j < KT; ++j)  // block-local rank, finished by route_slots
-      a.slots[t * KT + j] = __popcll(tokmask[pk[j]] & lt);
+  for (int i = 0; i < NP; ++i) {
+    const int j = sub + kSub * i;
+    if (active && j < KT) a.slots[t * KT + j] = __popcll(tokmask[pk[i]] & below);
   }
-  int32_t *bc = a.block_counts + (int64_t)blockIdx.x * P;
-  for (int p = tid; p < P; p += 256) bc[p] = __popcll(tokmask[p]);
+  for (int p = tid; p < P; p += 256)
+    a.block_counts[(int64_t)p * nblk + blk] = __popcll(tokmask[p]);
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
@@ -276,34 +410,35 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// One wave per physical expert: block counts -> exclusive block bases.
-__global__ __launch_bounds__(256) void route_block_scan(int32_t *bc, int32_t *counts, int nblk,
-                                                        int P) {
+// One wave per physical expert: its row of block counts -> exclusive block
+// prefixes (in place) and the expert's total.
+__global__ __launch_bounds__(256) void route_scan(int32_t *bc, int32_t *counts, int nblk, int P) {
   const int p = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (p >= P) return;
   const int l = lane_id();
+  int32_t *row = bc + (int64_t)p * nblk;
   int carry = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
-    int v[4];
+  for (int b0 = 0; b0 < nblk; b0 += 512) {
+    int v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int b = b0 + 64 * u + l;
-      v[u] = b < nblk ? bc[(int64_t)b * P + p] : 0;
+      v[u] = b < nblk ? row[b] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int b = b0 + 64 * u + l;
       const int incl = wave_inclusive_scan(v[u]);
-      if (b < nblk) bc[(int64_t)b * P + p] = carry + incl - v[u];
+      if (b < nblk) row[b] = carry + incl - v[u];
       carry += __shfl(incl, 63);
     }
   }
   if (l == 0) counts[p] = carry;
 }
 
-// Entries -> slots; the last block also scans counts into offsets and
+// Entries -> slots; the last workgroup also scans counts into offsets and
 // counts the drops (LDS-staged block scan).
-__global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries) {
+__global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries, int nblk) {
   const int tid = threadIdx.x;
   if (blockIdx.x == gridDim.x - 1) {
     __shared__ int wave_tot[4];
@@ -344,16 +479,16 @@ __global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries)
   if (i >= entries) return;
   const int64_t t = i / a.K;
   const int p = a.topk_ids[i];
-  const int j = a.block_counts[(t / kRouteTokens) * a.P + p] + a.slots[i];
+  const int j = a.block_counts[(int64_t)p * nblk + t / kRouteTokens] + a.slots[i];
   a.slots[i] = j < a.cap[p] ? a.capbase[p] + j : -1;
 }
 
 template <int KR>
-hipError_t launch_topk(const RouteArgs &a, int nblk, hipStream_t s) {
+hipError_t launch_topk(const RouteArgs &a, int nblk, int idbits, hipStream_t s) {
   if (a.shared)
-    route_topk_rank<KR, true><<<nblk, 256, 0, s>>>(a);
+    route_topk<KR, true><<<nblk, 256, 0, s>>>(a, idbits, nblk);
   else
-    route_topk_rank<KR, false><<<nblk, 256, 0, s>>>(a);
+    route_topk<KR, false><<<nblk, 256, 0, s>>>(a, idbits, nblk);
   return hipGetLastError();
 }
 
@@ -363,10 +498,12 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
   const int nblk = (a.T + kRouteTokens - 1) / kRouteTokens;
   hipError_t e = hipSuccess;
   if (nblk > 0) {
+    int idbits = 0;
+    while ((1 << idbits) < a.E) ++idbits;
     switch (a.KR) {
-#define MOEDC_CASE(k) \
-  case k:             \
-    e = launch_topk<k>(a, nblk, s); \
+#define MOEDC_CASE(k)                       \
+  case k:                                   \
+    e = launch_topk<k>(a, nblk, idbits, s); \
     break;
       MOEDC_CASE(1) MOEDC_CASE(2) MOEDC_CASE(3) MOEDC_CASE(4) MOEDC_CASE(5) MOEDC_CASE(6)
       MOEDC_CASE(7) MOEDC_CASE(8) MOEDC_CASE(9) MOEDC_CASE(10) MOEDC_CASE(11) MOEDC_CASE(12)
@@ -377,12 +514,12 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
   }
-  // counts: zero when no block ran.
-  route_block_scan<<<(a.P + 3) / 4, 256, 0, s>>>(a.block_counts, a.counts, nblk, a.P);
+  // counts: zero when no workgroup ran.
+  route_scan<<<(a.P + 3) / 4, 256, 0, s>>>(a.block_counts, a.counts, nblk, a.P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t entries = (int64_t)a.T * a.K;
   const int64_t grid = (entries + 255) / 256 + 1;
-  route_slots<<<(unsigned)grid, 256, 0, s>>>(a, entries);
+  route_slots<<<(unsigned)grid, 256, 0, s>>>(a, entries, nblk);
   return hipGetLastError();
 }
 

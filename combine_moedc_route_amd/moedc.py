@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmoedc.so")
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = range(7)
 SCORE_SOFTMAX, SCORE_SIGMOID_NORM = 0, 1
 FMT_BF16, FMT_Q8 = 0, 1
+DEAL_LPT, DEAL_ROUND_ROBIN = 0, 1
 
 # Every symbol include/moedc.h declares.
 EXPORTS = (
@@ -27,7 +28,7 @@ EXPORTS = (
     "moedc_combine", "moedc_route_dispatch", "moedc_combine_limited",
     "moedc_expert_stub", "moedc_expert_w8a8", "moedc_place_replicas",
     "moedc_lpt_partition", "moedc_status_string", "moedc_last_hip_error",
-    "moedc_route_noalloc",
+    "moedc_route_noalloc", "moedc_expert_w8a8_dealt",
 )
 
 
@@ -112,6 +113,8 @@ def load_library(path):
     L.moedc_combine_limited.restype = i32
     L.moedc_expert_w8a8.argtypes = [P, P, P, P, P, P, P, P]
     L.moedc_expert_w8a8.restype = i32
+    L.moedc_expert_w8a8_dealt.argtypes = [P, P, P, P, P, P, P, i32, P, P]
+    L.moedc_expert_w8a8_dealt.restype = i32
     L.moedc_expert_stub.argtypes = [P, P, P, P, P, P]
     L.moedc_expert_stub.restype = i32
     L.moedc_place_replicas.argtypes = [i32, P, i32, i32, P]
@@ -353,6 +356,24 @@ class Plan:
         _check(lib().moedc_expert_w8a8(self._h, _ptr(counts), _ptr(dispatch_buf), _ptr(weights),
                                        _ptr(w_scale), _ptr(combine_buf), _ptr(workspace),
                                        _stream(stream)), "moedc_expert_w8a8")
+
+    def expert_w8a8_dealt(self, counts, dispatch_buf, weights, w_scale, combine_buf, workspace,
+                          dealing: int, xcd_tiles=None, stream=None):
+        """moedc_expert_w8a8 with the band dealing chosen; xcd_tiles (int32
+        [8] on the device, optional) receives the tiles dealt to each die."""
+        s, H, P = self.sizes, self.hidden, self.num_phys
+        _need(counts, "counts", P, itemsize=4)
+        _need(dispatch_buf, "dispatch_buf", nbytes=s.dispatch_buf_bytes)
+        _need(weights, "weights", P * H * H, itemsize=1)
+        _need(w_scale, "w_scale", P * H, itemsize=4)
+        _need(combine_buf, "combine_buf", nbytes=s.combine_buf_bytes)
+        _need(workspace, "workspace", nbytes=s.workspace_bytes)
+        if xcd_tiles is not None:
+            _need(xcd_tiles, "xcd_tiles", 8, itemsize=4)
+        _check(lib().moedc_expert_w8a8_dealt(self._h, _ptr(counts), _ptr(dispatch_buf),
+                                             _ptr(weights), _ptr(w_scale), _ptr(combine_buf),
+                                             _ptr(workspace), dealing, _ptr(xcd_tiles),
+                                             _stream(stream)), "moedc_expert_w8a8_dealt")
 
     def expert_stub(self, counts, dispatch_buf, combine_buf, workspace, stream=None):
         s = self.sizes

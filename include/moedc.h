@@ -55,6 +55,14 @@ typedef enum moedc_score_fn {
   MOEDC_SCORE_SIGMOID_NORM = 1
 } moedc_score_fn;
 
+typedef enum moedc_xcd_dealing {
+  /* the expert layer's bands go to the accelerator dies (XCDs) by an LPT
+   * list schedule on their tile counts */
+  MOEDC_DEAL_LPT = 0,
+  /* band k to die k mod 8 (for comparison) */
+  MOEDC_DEAL_ROUND_ROBIN = 1
+} moedc_xcd_dealing;
+
 typedef enum moedc_elem_fmt {
   MOEDC_FMT_BF16 = 0,  /* expert outputs: [total_slots][hidden] BF16 rows */
   MOEDC_FMT_Q8 = 1     /* expert outputs in the dispatch slot layout (INT8 + scales) */
@@ -277,13 +285,36 @@ moedc_status moedc_expert_stub(const moedc_plan *plan, const int32_t *counts,
  * reading q and s_x in place from dispatch_buf.  weights: int8
  * [E_phys][H][H] (row n = output channel); w_scale: fp32 [E_phys][H];
  * combine_buf: BF16 [total_slots][H]; all 16-byte aligned.  Other rows of
- * combine_buf are not written.  Runs on int8 MFMA.
+ * combine_buf are not written.  Runs on int8 MFMA.  The work is cut into
+ * bands (4 x 256 output channels x all slot rows of one expert), which are
+ * dealt to the GPU's 8 dies by an LPT schedule built on the device from
+ * counts, as moedc_expert_w8a8_dealt with MOEDC_DEAL_LPT.
  * Errors: INVALID_ARG, ALIGN, HIP.
  */
 moedc_status moedc_expert_w8a8(const moedc_plan *plan, const int32_t *counts,
                                const void *dispatch_buf, const int8_t *weights,
                                const float *w_scale, uint16_t *combine_buf,
                                void *workspace, hipStream_t stream);
+
+/*
+ * moedc_expert_w8a8 with a choice of how the bands reach the dies
+ * ("StrataCL 深度技术分析", section 3.5: workload-balanced partitioning of
+ * expert-major work by an LPT list scheduler; here the workers are the 8
+ * XCDs of one GPU, each walking its band list with 32 workgroups).
+ * dealing: MOEDC_DEAL_LPT -- bands with tiles, longest first (equal tile
+ * counts in band order), each to the die with the fewest tiles so far
+ * (ties to the lower die); the largest die load is at most (4/3 - 1/24)
+ * times the best possible.  MOEDC_DEAL_ROUND_ROBIN -- band k to die k mod 8.
+ * The schedule is built on the device from counts, so the call can be
+ * captured in a graph.  xcd_tiles: device int32 [8] receiving the tiles
+ * dealt to each die, or NULL.  Results are identical for either dealing.
+ * Errors: INVALID_ARG (also for an unknown dealing), ALIGN, HIP.
+ */
+moedc_status moedc_expert_w8a8_dealt(const moedc_plan *plan, const int32_t *counts,
+                                     const void *dispatch_buf, const int8_t *weights,
+                                     const float *w_scale, uint16_t *combine_buf,
+                                     void *workspace, int32_t dealing, int32_t *xcd_tiles,
+                                     hipStream_t stream);
 
 /*
  * Load-proportional placement of redundant experts ("Decode Phase" of the
