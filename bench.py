@@ -21,6 +21,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -92,18 +93,23 @@ def source_sha(rels):
     return h.hexdigest()[:16]
 
 
+def progress(msg):
+    """One line on stderr when a leg of the benchmark ends (the JSON line
+    alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def measured_traffic(kernel, workload="global"):
-    """HBM bytes per launch from committed PMC runs, or None if the kernel
-    source changed since they were taken or they were taken on another
-    workload (the bytes of a launch depend on its shape)."""
+    """HBM bytes per launch of `kernel` on `workload` from committed PMC
+    runs, or None if none were taken on that workload or the kernel's
+    source changed since (the bytes of a launch depend on its code and
+    shape)."""
     try:
         with open(TRAFFIC_FILE) as f:
-            d = json.load(f)[kernel]
-    except (OSError, KeyError, ValueError):
+            d = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
-        return None
-    if d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -176,16 +182,18 @@ def cpu_baseline(tokens=30720, reps=3):
                       f"{sum(t_r) + sum(t_d) + sum(t_c):.1f} s timed in all)"}
 
 
-def run(args):
+def measure_path(wl, steps, warmup, fmt_name="bf16"):
+    """Time route + dispatch + combine on workload `wl` over `steps` steps
+    (after `warmup`), alternating two static dispatch/combine buffer sets;
+    the stand-in expert fills both combine sets once, untimed.  Returns the
+    numbers and the state the other legs reuse."""
     import numpy as np
     import torch
 
     from combine_moedc_route_amd import moedc as M
     from combine_moedc_route_amd import workloads as W
 
-    wl = W.get(args.workload)
     T, H, K, E = wl.tokens, wl.hidden, wl.K, wl.num_logical
-    torch.cuda.set_device(0)
     dev = "cuda:0"
     plan = M.Plan.from_workload(wl)
     s = plan.sizes
@@ -207,7 +215,7 @@ def run(args):
         sets.append((torch.empty(s.dispatch_buf_bytes, dtype=torch.uint8, device=dev),
                      torch.empty((s.total_slots, H), dtype=torch.int16, device=dev)))
     y = torch.empty((T, H), dtype=torch.int16, device=dev)
-    fmt = M.FMT_Q8 if args.combine_fmt == "q8" else M.FMT_BF16
+    fmt = M.FMT_Q8 if fmt_name == "q8" else M.FMT_BF16
 
     def route():
         plan.route(lg, ids, w, counts, offsets, slots, dropped, ws)
@@ -234,22 +242,21 @@ def run(args):
         if ev:
             ev[3].record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, evs[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = start.elapsed_time(stop) / steps
     r_us = [1e3 * e[0].elapsed_time(e[1]) for e in evs]
     d_us = [1e3 * e[1].elapsed_time(e[2]) for e in evs]
     c_us = [1e3 * e[2].elapsed_time(e[3]) for e in evs]
@@ -260,30 +267,9 @@ def run(args):
     comb_gbps = cb / (mean(c_us) * 1e-6) / 1e9
     disp_gbps = ab["dispatch"] / (mean(d_us) * 1e-6) / 1e9
     dc_gbps = (ab["dispatch"] + cb) / (dc_us * 1e-6) / 1e9
-    # Dominant kernel: the one with the larger mean duration.
-    dom = "combine" if mean(c_us) >= mean(d_us) else "dispatch"
-    dom_bytes, dom_gbps = (cb, comb_gbps) if dom == "combine" else (ab["dispatch"], disp_gbps)
-    traffic = measured_traffic(dom, wl.name) if fmt == M.FMT_BF16 else None
-    res = {
-        "metric": METRIC,
-        "value": T / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    out = {
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16 in/out, int8 payload + fp32 scales, fp32 accumulate",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{wl.name}: {wl.description}",
-            "tokens": T, "hidden": H, "experts": wl.num_phys, "top_k": K,
-            "group": 128, "capacity_per_expert": int(wl.capacity[0]),
-            "combine_input": "bf16" if fmt == M.FMT_BF16 else "q8",
-            "step": "route + dispatch + combine, buffer sets alternating",
-        },
+        "tokens_per_s": T / (ms_per_step * 1e-3),
         "route_us": mean(r_us),
         "dispatch_us": mean(d_us),
         "combine_us": mean(c_us),
@@ -299,17 +285,64 @@ def run(args):
         "dispatch_plus_combine_frac_of_hbm_peak": dc_gbps / HBM_PEAK_GBPS,
         "dispatch_frac_of_hbm_peak": disp_gbps / HBM_PEAK_GBPS,
         "combine_frac_of_hbm_peak": comb_gbps / HBM_PEAK_GBPS,
+        "route_GBps": ab["route"] / (mean(r_us) * 1e-6) / 1e9,
+        "route_frac_of_hbm_peak": ab["route"] / (mean(r_us) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes": {"dispatch": ab["dispatch"], "combine": cb, "route": ab["route"]},
-        "roofline": {
-            "kernel": dom,
-            "bound": "hbm",
-            "achieved": dom_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": dom_gbps / HBM_PEAK_GBPS,
-            "traffic": traffic,
-        },
         "wall_s_timed": wall,
+    }
+    state = dict(plan=plan, wl=wl, counts=counts, sets=sets, ws=ws, xd=xd, slots=slots, w=w,
+                 y=y, fmt=fmt, ab=ab, cb=cb)
+    return out, state
+
+
+def run(args):
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+
+    wl = W.get(args.workload)
+    T, H, K = wl.tokens, wl.hidden, wl.K
+    torch.cuda.set_device(0)
+    m, st = measure_path(wl, args.steps, args.warmup, args.combine_fmt)
+    progress(f"{wl.name}: {m['ms_per_step']:.4f} ms per step")
+    fmt, ab, cb = st["fmt"], st["ab"], st["cb"]
+    plan, sets, slots, w, y = st["plan"], st["sets"], st["slots"], st["w"], st["y"]
+    # Dominant kernel: the one with the larger mean duration.
+    dom = "combine" if m["combine_us"] >= m["dispatch_us"] else "dispatch"
+    dom_bytes, dom_gbps = ((cb, m["combine_GBps"]) if dom == "combine"
+                           else (ab["dispatch"], m["dispatch_GBps"]))
+    traffic = measured_traffic(dom, wl.name) if fmt == M.FMT_BF16 else None
+    res = {
+        "metric": METRIC,
+        "value": m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in/out, int8 payload + fp32 scales, fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "tokens": T, "hidden": H, "experts": wl.num_phys, "top_k": K,
+            "group": 128, "capacity_per_expert": int(wl.capacity[0]),
+            "combine_input": "bf16" if fmt == M.FMT_BF16 else "q8",
+            "step": "route + dispatch + combine, buffer sets alternating",
+        },
+    }
+    res.update({k: v for k, v in m.items() if k not in ("ms_per_step", "tokens_per_s")})
+    res["roofline"] = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": dom_gbps,
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": dom_gbps / HBM_PEAK_GBPS,
+        "traffic": traffic,
     }
     if fmt == M.FMT_BF16:
         # The same combine reading the INT8 dispatch slots (identity experts /
@@ -324,20 +357,46 @@ def run(args):
                 cq.append((e0, e1))
         torch.cuda.synchronize()
         q_us = [1e3 * e0.elapsed_time(e1) for e0, e1 in cq]
+        mean = statistics.fmean
         q_gbps = ab["combine_q8"] / (mean(q_us) * 1e-6) / 1e9
         res["combine_q8"] = {"us": mean(q_us), "us_median": statistics.median(q_us),
                              "GBps": q_gbps, "frac_of_hbm_peak": q_gbps / HBM_PEAK_GBPS,
                              "algorithmic_bytes": ab["combine_q8"]}
+    if args.workload == "global" and not args.no_ceilings:
+        res["ceilings"] = ceilings(st, m)
+        progress("ceilings")
     if args.workload == "global" and not args.no_expert:
-        res["expert_gemm"] = expert_gemm(plan, wl, counts, sets[0][0], sets[0][1], ws, xd, slots)
+        res["expert_gemm"] = expert_gemm(plan, wl, st["counts"], sets[0][0], sets[0][1],
+                                         st["ws"], st["xd"], slots)
+        progress("expert_gemm")
+    del st, sets
+    torch.cuda.empty_cache()
+    if args.workload == "global" and not args.no_workloads:
+        # The other large configurations, each on its own buffers.
+        for name in ("skewed", "prefill"):
+            sub, sst = measure_path(W.get(name), max(10, args.steps // 4), 5)
+            sub["workload"] = f"{name}: {W.get(name).description}"
+            sub["roofline_traffic"] = {k: measured_traffic(k, name) for k in ("dispatch", "combine")}
+            res[name] = sub
+            progress(f"{name}: {sub['ms_per_step']:.4f} ms per step")
+            del sst
+            torch.cuda.empty_cache()
+    if args.workload == "global" and not args.no_expert:
+        res["expert_lpt"] = expert_lpt()
+        progress("expert_lpt")
+        torch.cuda.empty_cache()
     if args.workload == "global" and not args.no_decode:
         res["decode_latency"] = decode_latency()
         # Batches of one token per wave or fewer take the one-launch route.
         res["decode_latency"]["small_batches"] = {
             str(n): decode_latency(tokens=n, which=("route", "route_dispatch_fused", "fused_step"))
             for n in (1, 16)}
+        progress("decode_latency")
+        res["overlap"] = overlap()
+        progress("overlap")
     if args.workload == "global" and not args.no_placement:
         res["placement"] = placement()
+        progress("placement")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
     print(json.dumps(res), flush=True)
@@ -509,6 +568,258 @@ def library_int8_gemm(wl, counts, dbuf, Wd, slot_stride, iters):
     return 1e3 * e0.elapsed_time(e1) / iters
 
 
+def _ceiling_lib():
+    import ctypes as C
+    L = C.CDLL(os.path.join(ROOT, "combine_moedc_route_amd", "libmoedc_ceiling.so"))
+    P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+    L.moedc_ceiling_read.argtypes = [P, i64, P, P]
+    L.moedc_ceiling_write.argtypes = [P, i64, P]
+    L.moedc_ceiling_copy.argtypes = [P, P, i64, P]
+    L.moedc_ceiling_scatter.argtypes = [P, i32, i32, P, i64, i32, P]
+    L.moedc_ceiling_gather.argtypes = [P, P, i32, i32, i64, i32, P, P]
+    for f in ("read", "write", "copy", "scatter", "gather"):
+        getattr(L, "moedc_ceiling_" + f).restype = i32
+    return L
+
+
+def _time_us(fn, iters=10, warm=3):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / iters
+
+
+def ceilings(st, m, stream_bytes=4 << 30):
+    """What the memory system gives (libmoedc_ceiling kernels, on the
+    current stream): 4 GiB streaming read, write and copy, and the exact
+    access patterns of the global batch's dispatch (stores of each token's
+    K slots, 7424 bytes each, without reading x or quantizing) and combine
+    (each token's K BF16 rows read, one row written, without arithmetic).
+    Dispatch and combine are read against these as well as 8 TB/s."""
+    import torch
+    L = _ceiling_lib()
+    wl, plan, slots = st["wl"], st["plan"], st["slots"]
+    T, H, K = wl.tokens, wl.hidden, wl.K
+    sz = plan.sizes
+    cs = torch.cuda.current_stream().cuda_stream
+    a = torch.empty(stream_bytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(stream_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a.fill_(1)
+
+    def ok(rc):
+        if rc:
+            raise RuntimeError(f"ceiling kernel failed: hip error {rc}")
+
+    res = {}
+    us = _time_us(lambda: ok(L.moedc_ceiling_read(a.data_ptr(), stream_bytes, sink.data_ptr(), cs)))
+    res["read"] = {"bytes": stream_bytes, "us": us, "GBps": stream_bytes / us / 1e3}
+    us = _time_us(lambda: ok(L.moedc_ceiling_write(b.data_ptr(), stream_bytes, cs)))
+    res["write"] = {"bytes": stream_bytes, "us": us, "GBps": stream_bytes / us / 1e3}
+    us = _time_us(lambda: ok(L.moedc_ceiling_copy(b.data_ptr(), a.data_ptr(), stream_bytes, cs)))
+    res["copy"] = {"bytes": 2 * stream_bytes, "us": us, "GBps": 2 * stream_bytes / us / 1e3}
+    del a, b
+    torch.cuda.empty_cache()
+    G = H // 128
+    row = H + 4 * (-(-G // 32) * 32)            # the bytes dispatch writes per slot (padding included)
+    dbuf, cbuf = st["sets"][0]
+    kept = int((slots >= 0).sum().item())
+    us = _time_us(lambda: ok(L.moedc_ceiling_scatter(slots.data_ptr(), T, K, dbuf.data_ptr(),
+                                                     sz.slot_stride, row, cs)))
+    res["dispatch_scatter"] = {"bytes": kept * row, "us": us, "GBps": kept * row / us / 1e3,
+                               "what": "dispatch's stores alone (each token's K slots, "
+                                       f"{row} B each), no x read, no quantization"}
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    gb = kept * 2 * H + 2 * T * H
+    us = _time_us(lambda: ok(L.moedc_ceiling_gather(cbuf.data_ptr(), slots.data_ptr(), T, K,
+                                                    2 * H, 2 * H, out.data_ptr(), cs)))
+    res["combine_gather"] = {"bytes": gb, "us": us, "GBps": gb / us / 1e3,
+                             "what": "combine's BF16 row reads and output writes alone, "
+                                     "no weights, no arithmetic"}
+    # The path's kernels against these ceilings (algorithmic bytes / time).
+    res["dispatch_frac_of_scatter_plus_read"] = None
+    res["combine_frac_of_gather"] = m["combine_GBps"] / res["combine_gather"]["GBps"]
+    # dispatch = its stores + reading x: against the scatter pattern plus a
+    # streaming read of x at the read ceiling.
+    t_ideal = res["dispatch_scatter"]["us"] + 2 * T * H / res["read"]["GBps"] / 1e3
+    res["dispatch_frac_of_scatter_plus_read"] = t_ideal / m["dispatch_us"]
+    res["dispatch_frac_of_copy"] = m["dispatch_GBps"] / res["copy"]["GBps"]
+    res["combine_frac_of_copy"] = m["combine_GBps"] / res["copy"]["GBps"]
+    return res
+
+
+def expert_lpt(iters=5):
+    """The expert layer on the skewed batch (Zipf(1.1), 256 logical experts,
+    30720 tokens, top-8, hidden 7168) with the bands of its work dealt to
+    the 8 XCDs round-robin and by the device-built LPT schedule, under two
+    replica tables: the workload's own (the 32 most popular experts get one
+    extra copy) and one from moedc_place_replicas on the batch's loads.
+    Tiles per XCD are the device's own schedule (xcd_tiles output)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+    base = W.get("skewed")
+    T, H, E = base.tokens, base.hidden, base.num_logical
+    x, logits = W.make_inputs(base)
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    lg = torch.from_numpy(logits).cuda()
+    del x
+    P = base.num_phys
+    gen = torch.Generator(device="cuda").manual_seed(71)
+    Wd = torch.randint(-127, 128, (P, H, H), dtype=torch.int8, device="cuda", generator=gen)
+    wsd = (torch.rand((P, H), device="cuda", generator=gen) + 0.5) / (127.0 * H ** 0.5)
+
+    def route_counts(wl):
+        plan = M.Plan.from_workload(dataclasses.replace(wl, hidden=128))
+        b = plan.alloc("cuda:0")
+        plan.route(lg, b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"],
+                   b["dropped"], b["workspace"])
+        return b["counts"].cpu().numpy()
+
+    ident = dataclasses.replace(base, num_phys=E, capacity=np.full(E, T, np.int32),
+                                replica_table=None)
+    load = route_counts(ident).astype(np.float64)
+    table = M.place_replicas(load, P - E, 8)
+    planned = dataclasses.replace(base, capacity=np.full(P, T, np.int32), replica_table=table)
+    cnt = route_counts(planned)
+    planned.capacity = ((cnt + 64 + 63) // 64 * 64).astype(np.int32)
+    res = {"workload": f"skewed: {base.description}", "weights": "int8 U[-127,127], torch seed 71",
+           "what": "expert_w8a8 over every occupied slot; bands of 4 x 256 channels x all rows "
+                   "of one expert dealt to the 8 XCDs"}
+    for tname, wl in (("fixed_table", base), ("planned_table", planned)):
+        plan = M.Plan.from_workload(wl)
+        b = plan.alloc("cuda:0")
+        plan.route(lg, b["topk_ids"], b["topk_w"], b["counts"], b["offsets"], b["slots"],
+                   b["dropped"], b["workspace"])
+        plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+        torch.cuda.synchronize()
+        assert int(b["dropped"].item()) == 0
+        used = torch.minimum(b["counts"], torch.from_numpy(wl.capacity).cuda()).sum().item()
+        ops = 2.0 * used * H * H
+        sub = {"rows": int(used), "largest_copy_rows": int(b["counts"].max().item())}
+        outs = {}
+        for dname, deal in (("round_robin", M.DEAL_ROUND_ROBIN), ("lpt", M.DEAL_LPT)):
+            xt = torch.zeros(8, dtype=torch.int32, device="cuda")
+            f = lambda: plan.expert_w8a8_dealt(b["counts"], b["dispatch_buf"], Wd, wsd,
+                                               b["combine_buf"], b["workspace"], deal, xt)
+            us = _time_us(f, iters=iters, warm=1)
+            tiles = xt.cpu().numpy()
+            outs[dname] = b["combine_buf"].clone() if dname == "round_robin" else None
+            sub[dname] = {"us": us, "TOPs": ops / (us * 1e-6) / 1e12,
+                          "frac_of_int8_peak": ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS,
+                          "xcd_tiles": tiles.tolist(),
+                          "max_over_mean": float(tiles.max() / tiles.mean())}
+        sub["outputs_identical"] = bool(torch.equal(outs["round_robin"], b["combine_buf"]))
+        sub["lpt_gain"] = sub["round_robin"]["us"] / sub["lpt"]["us"] - 1.0
+        res[tname] = sub
+        del plan, b, outs
+        torch.cuda.empty_cache()
+    del Wd
+    torch.cuda.empty_cache()
+    return res
+
+
+def overlap(rounds=20):
+    """moedc_combine_limited on 16 workgroups (the 96-token decode batch,
+    BF16 expert outputs) beside the expert layer of another batch (3000
+    tokens, hidden 1152, 40 experts) on a second stream, both at the default
+    priority: one round run serially on one stream, and with the two on two
+    streams; also with the uncapped combine.  Mean device time per round
+    between events on the launching stream."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+    wa = W.get("decode")
+    pa = M.Plan.from_workload(wa)
+    ba = pa.alloc("cuda:0")
+    xa, la = W.make_inputs(wa)
+    pa.route(torch.from_numpy(la).cuda(), ba["topk_ids"], ba["topk_w"], ba["counts"],
+             ba["offsets"], ba["slots"], ba["dropped"], ba["workspace"])
+    pa.dispatch(torch.from_numpy(xa.view(np.int16)).cuda(), ba["slots"], ba["dispatch_buf"])
+    pa.expert_stub(ba["counts"], ba["dispatch_buf"], ba["combine_buf"], ba["workspace"])
+    ya = torch.empty((wa.tokens, wa.hidden), dtype=torch.int16, device="cuda")
+    wb = dataclasses.replace(W.with_tokens(W.get("ragged"), 3000),
+                             capacity=np.full(40, 470, np.int32))
+    pb = M.Plan.from_workload(wb)
+    bb = pb.alloc("cuda:0")
+    xb, lb = W.make_inputs(wb)
+    pb.route(torch.from_numpy(lb).cuda(), bb["topk_ids"], bb["topk_w"], bb["counts"],
+             bb["offsets"], bb["slots"], bb["dropped"], bb["workspace"])
+    pb.dispatch(torch.from_numpy(xb.view(np.int16)).cuda(), bb["slots"], bb["dispatch_buf"])
+    Wt, wsc = W.make_expert_weights(61, wb.num_phys, wb.hidden)
+    Wd, wsd = torch.from_numpy(Wt).cuda(), torch.from_numpy(wsc).cuda()
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def comb(stream, cap):
+        if cap:
+            pa.combine_limited(ba["combine_buf"], M.FMT_BF16, ba["slots"], ba["topk_w"], ya, 16,
+                               stream=stream)
+        else:
+            pa.combine(ba["combine_buf"], M.FMT_BF16, ba["slots"], ba["topk_w"], ya,
+                       stream=stream)
+
+    def expert(stream):
+        pb.expert_w8a8(bb["counts"], bb["dispatch_buf"], Wd, wsd, bb["combine_buf"],
+                       bb["workspace"], stream=stream)
+
+    def timed(body):
+        """Mean us per round of `body(rounds)`, which issues all rounds."""
+        body(3)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        body(rounds)
+        e1.record(main)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / rounds
+
+    def serial(cap, n):
+        for _ in range(n):
+            comb(main, cap)
+            expert(main)
+
+    def parallel(cap, n):
+        # every round's combine on one stream, every expert layer on the
+        # other, joined once at the end
+        s1.wait_stream(main)
+        s2.wait_stream(main)
+        for _ in range(n):
+            comb(s1, cap)
+        for _ in range(n):
+            expert(s2)
+        main.wait_stream(s1)
+        main.wait_stream(s2)
+
+    res = {"what": "combine of the 96-token decode batch beside the expert layer of a "
+                   "3000-token batch (hidden 1152, 40 experts); mean us per round over "
+                   f"{rounds} rounds issued back to back (two streams joined once)",
+           "combine_16wg_alone_us": timed(lambda n: [comb(main, True) for _ in range(n)]),
+           "combine_alone_us": timed(lambda n: [comb(main, False) for _ in range(n)]),
+           "expert_alone_us": timed(lambda n: [expert(main) for _ in range(n)])}
+    for cap, name in ((True, "capped_16wg"), (False, "uncapped")):
+        res[name] = {"serial_us": timed(lambda n: serial(cap, n)),
+                     "two_streams_us": timed(lambda n: parallel(cap, n))}
+        res[name]["saved_us"] = res[name]["serial_us"] - res[name]["two_streams_us"]
+    return res
+
+
 def placement(workers=8, redundant=32, max_replicas=8):
     """Load balancing on the skewed workload (Zipf(1.1) popularity over 256
     experts, top-8, 30720 tokens): per-expert loads from the device route,
@@ -632,10 +943,18 @@ def summarize_rocprof(d, out):
     print(text)
 
 
-def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes,
-                   required=("combine", "dispatch", "route", "expert_gemm")):
-    """Per-launch HBM bytes of each kernel from FETCH_SIZE / WRITE_SIZE runs,
-    each counter scaled by what it reads for a plain copy of known size."""
+# Kernel of each path step in a one-workload bench run (name patterns):
+# combine on BF16 expert outputs, dispatch with a workgroup per token, the
+# route's top-k kernel and the expert layer's GEMM.
+TRAFFIC_TAGS = {"combine": r"combine_kernel<\d+, false,", "dispatch": r"dispatch_token_block<false>",
+                "route": r"route_topk<", "expert_gemm": r"expert_gemm<true>\("}
+
+
+def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+    """Per-launch HBM bytes of each kernel of one workload's bench run from
+    its FETCH_SIZE and WRITE_SIZE runs, each counter scaled by what it reads
+    for a plain copy of known size; merged into the committed table under
+    the workload's name."""
     import csv
 
     def per_kernel(d, counter):
@@ -654,32 +973,34 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_by
     ff = copy_factor(copy_fetch_dir, "FETCH_SIZE")
     fw = copy_factor(copy_write_dir, "WRITE_SIZE")
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    out = {"_about": "HBM bytes per launch on the global workload from rocprofv3 "
-                     f"FETCH_SIZE x{ff:.4f} and WRITE_SIZE x{fw:.4f} (scales from a plain "
-                     f"{copy_bytes}-byte copy); valid while source_sha matches."}
-    # Kernels of the global workload's launches: combine with one wave per
-    # 512-value chunk on 16-wave workgroups (BF16 input), dispatch with a
-    # workgroup per token; the tags are name prefixes, so extra trailing
-    # template arguments match.
-    missing = []
-    for key, tag in (("combine", "combine_kernel<8, false, 16, 1>"),
-                     ("dispatch", "dispatch_token_block<false>"),
-                     ("route", "route_topk_rank<8, false>"), ("expert_gemm", "expert_gemm<true>(")):
-        kf = [k for k in fetch if tag in k]
-        kw = [k for k in write if tag in k]
-        if not kf or not kw:
-            missing.append(key)
+    entry = {}
+    for key, tag in TRAFFIC_TAGS.items():
+        kf = [k for k in fetch if re.search(tag, k)]
+        kw = [k for k in write if re.search(tag, k)]
+        if len(kf) != 1 or len(kw) != 1:
+            if kf or kw:
+                raise SystemExit(f"record_traffic: {key}: expected one kernel matching {tag!r}, "
+                                 f"found {kf} / {kw}; nothing written")
             continue
-        out[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]), "workload": "global",
-                    "fetch_bytes": fetch[kf[0]] * ff, "write_bytes": write[kw[0]] * fw,
-                    "bytes_per_launch": fetch[kf[0]] * ff + write[kw[0]] * fw}
-    missing = [k for k in missing if k in required]
-    if missing:
-        raise SystemExit(f"record_traffic: no counter rows for {missing} in {fetch_dir} / "
+        entry[key] = {"source_sha": source_sha(KERNEL_SOURCES[key]), "kernel": kf[0][:120],
+                      "fetch_bytes": fetch[kf[0]] * ff, "write_bytes": write[kw[0]] * fw,
+                      "bytes_per_launch": fetch[kf[0]] * ff + write[kw[0]] * fw}
+    if "combine" not in entry or "dispatch" not in entry:
+        raise SystemExit(f"record_traffic: no combine/dispatch counter rows in {fetch_dir} / "
                          f"{write_dir}; nothing written")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            out = json.load(f)
+    except (OSError, ValueError):
+        out = {}
+    out = {k: v for k, v in out.items() if isinstance(v, dict) and "source_sha" not in v}
+    out["_about"] = ("HBM bytes per launch, by workload and kernel, from rocprofv3 FETCH_SIZE "
+                     "and WRITE_SIZE runs scaled by what each counter reads for a plain "
+                     f"{copy_bytes}-byte copy; an entry is valid while its source_sha matches.")
+    out[workload] = {"fetch_scale": ff, "write_scale": fw, **entry}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
+    print(json.dumps(out[workload], indent=1))
 
 
 def main():
@@ -693,13 +1014,15 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-expert", action="store_true")
     ap.add_argument("--no-placement", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=30720)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=4 << 30)
     ap.add_argument("--summarize-rocprof", metavar="DIR")
-    ap.add_argument("--record-traffic", nargs=4,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--out")
     args = ap.parse_args()
     if args.record_traffic:

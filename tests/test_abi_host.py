@@ -15,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moedc.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moedc_[a-z0-9_]+)\s*\(", text)))
 
@@ -25,6 +25,17 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     names = declared_functions()
     assert set(names) == set(M.EXPORTS), names
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_ceiling_library_exports_every_declared_symbol():
+    """libmoedc_ceiling.so (the benchmark's bandwidth-ceiling kernels) loads
+    and exports what include/moedc_ceiling.h declares."""
+    names = declared_functions(os.path.join(ROOT, "include", "moedc_ceiling.h"))
+    assert names == ["moedc_ceiling_copy", "moedc_ceiling_gather", "moedc_ceiling_read",
+                     "moedc_ceiling_scatter", "moedc_ceiling_write"]
+    L = C.CDLL(os.path.join(ROOT, "combine_moedc_route_amd", "libmoedc_ceiling.so"))
     for n in names:
         assert getattr(L, n) is not None
 

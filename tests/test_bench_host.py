@@ -64,36 +64,49 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     tf = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
-    name = "void moedc::(anonymous namespace)::combine_kernel<8, false, 16, 1>(moedc::CombineArgs)"
+    comb = "void moedc::(anonymous namespace)::combine_kernel<8, false, 16, 1>(moedc::CombineArgs)"
+    comb_q8 = "void moedc::(anonymous namespace)::combine_kernel<8, true, 16, 1>(moedc::CombineArgs)"
+    disp = "void moedc::(anonymous namespace)::dispatch_token_block<false>(moedc::DispatchArgs)"
     _write_csv(str(tmp_path / "f" / "f_counter_collection.csv"), hdr,
-               [[name, "FETCH_SIZE", 1000.0], [name, "FETCH_SIZE", 1000.0]])
-    _write_csv(str(tmp_path / "w" / "w_counter_collection.csv"), hdr, [[name, "WRITE_SIZE", 500.0]])
+               [[comb, "FETCH_SIZE", 1000.0], [comb, "FETCH_SIZE", 1000.0],
+                [comb_q8, "FETCH_SIZE", 7.0], [disp, "FETCH_SIZE", 300.0]])
+    _write_csv(str(tmp_path / "w" / "w_counter_collection.csv"), hdr,
+               [[comb, "WRITE_SIZE", 500.0], [comb_q8, "WRITE_SIZE", 9.0],
+                [disp, "WRITE_SIZE", 100.0]])
     # A 4096-byte copy whose counters read 2 KiB fetched and 4 KiB written.
     _write_csv(str(tmp_path / "cf" / "c_counter_collection.csv"), hdr,
                [["__amd_rocclr_copyBuffer", "FETCH_SIZE", 2.0]])
     _write_csv(str(tmp_path / "cw" / "c_counter_collection.csv"), hdr,
                [["__amd_rocclr_copyBuffer", "WRITE_SIZE", 4.0]])
-    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
-                         str(tmp_path / "cw"), 4096, required=("combine",))
+    dirs = [str(tmp_path / d) for d in ("f", "w", "cf", "cw")]
+    bench.record_traffic("global", *dirs, 4096)
     d = json.loads(tf.read_text())
-    assert d["combine"]["fetch_bytes"] == 1000 * 1024 * 2.0
-    assert d["combine"]["write_bytes"] == 500 * 1024 * 1.0
-    assert d["combine"]["source_sha"] == bench.source_sha(bench.KERNEL_SOURCES["combine"])
-    assert "dispatch" not in d
+    g = d["global"]
+    # BF16 combine only (the Q8 kernel is another row), scaled by the copy.
+    assert g["combine"]["fetch_bytes"] == 1000 * 1024 * 2.0
+    assert g["combine"]["write_bytes"] == 500 * 1024 * 1.0
+    assert g["dispatch"]["bytes_per_launch"] == 300 * 1024 * 2.0 + 100 * 1024
+    assert g["combine"]["source_sha"] == bench.source_sha(bench.KERNEL_SOURCES["combine"])
+    assert "route" not in g
     # The recorded figure is served while the kernel source is unchanged...
     assert bench.measured_traffic("combine") == 1000 * 1024 * 2.0 + 500 * 1024
     # ...for the workload the counters were taken on only...
-    assert d["combine"]["workload"] == "global"
     assert bench.measured_traffic("combine", "prefill") is None
-    # ...and withheld once it changes.
-    d["combine"]["source_sha"] = "0" * 16
+    # ...and a second workload's run is merged beside the first.
+    bench.record_traffic("prefill", *dirs, 8192)
+    d = json.loads(tf.read_text())
+    assert set(d) == {"_about", "global", "prefill"}
+    assert bench.measured_traffic("combine", "prefill") == 2 * (1000 * 1024 * 2.0 + 500 * 1024)
+    # ...and withheld once the kernel changes.
+    d["global"]["combine"]["source_sha"] = "0" * 16
     tf.write_text(json.dumps(d))
     assert bench.measured_traffic("combine") is None
-    # A required kernel without counter rows is an error, and nothing is written.
+    assert bench.measured_traffic("dispatch") == 300 * 1024 * 2.0 + 100 * 1024
+    # Runs without combine and dispatch rows are an error, and nothing is written.
     tf.unlink()
+    _write_csv(str(tmp_path / "e" / "e_counter_collection.csv"), hdr, [["other", "FETCH_SIZE", 1.0]])
     with pytest.raises(SystemExit):
-        bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"),
-                             str(tmp_path / "cw"), 4096)
+        bench.record_traffic("global", str(tmp_path / "e"), *dirs[1:], 4096)
     assert not tf.exists()
 
 
