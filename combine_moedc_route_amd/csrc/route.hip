@@ -18,7 +18,11 @@
 //      = larger value, or the same high part and a lower id.  Each lane
 //      keeps its top KR + 1 keys sorted, one v_med3_u32 per list entry per
 //      logit (insertion is L[j] = med3(L[j-1], L[j], c), L[0] = max(L[0],
-//      c)), and the token's four lists merge through quad DPP.
+//      c)), and the token's four lists merge through quad DPP.  The kernel
+//      is bound by VALU issue, so rows of exactly 256 logits (one chunk)
+//      take a path with unguarded loads (compute starts on the first while
+//      the rest are in flight) and 5 instructions of key building per logit
+//      besides the 9 of the insertion.
 //    - Exactness.  Where the high parts (the key without the id bits) of
 //      the merged top KR + 1 strictly decrease, the first KR keys are the
 //      top KR logits by (value desc, id asc) in that order: every other
@@ -28,10 +32,11 @@
 //      ranked again on their own, by a second med3 pass keyed on the low b
 //      bits of ok (the part the packed key dropped) and the id -- exact,
 //      since the class shares h -- and fill the positions below the picks
-//      with higher high parts.  If only picks share a high part, their set
-//      is right and only their order needs the exact values, which are
-//      re-read for the gates anyway: the token's picks are then sorted by
-//      (ok desc, id asc).
+//      with higher high parts (one max per logit when only the last
+//      position is open).  If picks share a high part, their set is right
+//      and only their order needs the exact values, which are re-read for
+//      the gates anyway: each lane ranks its picks by (ok desc, id asc)
+//      against the token's others and writes them at that rank.
 //    - Gates, replica mapping, outputs; the token's bit in a per-expert
 //      64-bit mask in LDS (atomic OR, order free).  The block-local rank of
 //      an entry, the popcount of the lower bits of its expert's mask, goes
@@ -56,10 +61,12 @@ constexpr int kLaneCols = 64;     // columns per lane per chunk (256 per token)
 constexpr int kChunkCols = kSub * kLaneCols;
 static_assert(kRouteTokens * kSub == 256, "64 tokens x 4 lanes per workgroup");
 
-// Order-preserving integer image of a float; -0 and +0 map to one key.
+// Order-preserving integer image of a float; -0 and +0 map to one key
+// (adding +0 turns -0 into +0).  Negative floats get every bit flipped, the
+// others only the sign bit: an arithmetic shift makes the mask, no branch.
 __device__ __forceinline__ uint32_t okey(float v) {
   const uint32_t u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float okey_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -179,12 +186,43 @@ __device__ __forceinline__ uint32_t class_key(float x, int e, int E, uint32_t h,
   return (e < E && (k >> idbits) == h) ? (((k & idmask) << idbits) | (idmask - (uint32_t)e)) : 0u;
 }
 
+// The boundary class ranked over a lane's columns into the top NC class keys,
+// merged over the token's quad.  REG: the row (E <= 256) is still in v;
+// otherwise its chunks are read again from memory.
+template <int NC, bool REG>
+__device__ __forceinline__ void class_pass(uint32_t (&C)[NC], const float (&v)[kLaneCols],
+                                           const RouteArgs &a, int64_t t, int sub, bool vec4,
+                                           uint32_t h, int idbits, uint32_t idmask) {
+#pragma unroll
+  for (int j = 0; j < NC; ++j) C[j] = 0u;
+  if (REG) {
+#pragma unroll
+    for (int i = 0; i < kLaneCols; ++i)
+      list_insert<NC>(C, class_key(v[i], lane_col(0, sub, i), a.E, h, idbits, idmask));
+  } else {
+    for (int c0 = 0; c0 < a.E; c0 += kChunkCols) {
+#pragma unroll 1
+      for (int g = 0; g < kLaneCols / 16; ++g) {
+        float w[16];
+        load_group(w, a, t, c0, g, sub, vec4);
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          list_insert<NC>(C, class_key(w[u], lane_col(c0, sub, 16 * g + u), a.E, h, idbits,
+                                       idmask));
+      }
+    }
+  }
+  list_merge<NC, kDppQuadXor1>(C);
+  list_merge<NC, kDppQuadXor2>(C);
+}
+
 template <int KR, bool SHARED>
 __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int nblk) {
   constexpr int KT = KR + (SHARED ? 1 : 0);
   constexpr int N = KR + 1;                   // one key past the picks, for the exactness test
   constexpr int NP = (KT + kSub - 1) / kSub;  // picks per lane
   __shared__ unsigned long long tokmask[kMaxExperts];
+  __shared__ float sorted_s[kRouteTokens][KR];  // sigmoid numerators in pick order (ties only)
 
   const int tid = threadIdx.x;
   const int r = tid >> 2, sub = tid & 3;
@@ -202,13 +240,39 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
 #pragma unroll
   for (int j = 0; j < N; ++j) L[j] = 0u;  // below every real key
   float v[kLaneCols];
-  for (int c0 = 0; c0 < E; c0 += kChunkCols) {
-    load_chunk(v, a, t, active, c0, sub, vec4);
+  const bool full = E == kChunkCols;  // one chunk, every column in range
+  if (full) {
+    // Unguarded 16-byte loads (a padding token past T reads row T - 1 and is
+    // never written out), so the keys can start on the first loads while the
+    // rest are in flight.  A key is built as (ok | idmask) - (column within
+    // the lane's stripe); the lane's own offset 4 sub comes off the merged-in
+    // entries at the end, all of them real keys by then (N <= 64 inserted),
+    // which leaves each entry's low bits at idmask - e.
+    const int64_t tl = active ? t : (int64_t)a.T - 1;
+    const float4 *row = reinterpret_cast<const float4 *>(a.logits + tl * kChunkCols) + sub;
 #pragma unroll
-    for (int i = 0; i < kLaneCols; ++i) {
-      const int e = lane_col(c0, sub, i);
-      const uint32_t key = (okey(v[i]) & ~idmask) | (idmask - (uint32_t)e);
-      list_insert<N>(L, e < E ? key : 0u);
+    for (int i = 0; i < kLaneCols / 4; ++i) {
+      const float4 x = row[4 * i];
+      v[4 * i] = x.x;
+      v[4 * i + 1] = x.y;
+      v[4 * i + 2] = x.z;
+      v[4 * i + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < kLaneCols; ++i)
+      list_insert<N>(L, (okey(v[i]) | idmask) - (uint32_t)lane_col(0, 0, i));
+    const uint32_t off = 4u * (uint32_t)sub;
+#pragma unroll
+    for (int j = 0; j < N; ++j) L[j] -= off;
+  } else {
+    for (int c0 = 0; c0 < E; c0 += kChunkCols) {
+      load_chunk(v, a, t, active, c0, sub, vec4);
+#pragma unroll
+      for (int i = 0; i < kLaneCols; ++i) {
+        const int e = lane_col(c0, sub, i);
+        const uint32_t key = (okey(v[i]) & ~idmask) | (idmask - (uint32_t)e);
+        list_insert<N>(L, e < E ? key : 0u);
+      }
     }
   }
   list_merge<N, kDppQuadXor1>(L);
@@ -225,34 +289,28 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
   inner = inner && active;
 
   // ---- boundary class: rank the logits of high part hmin by their low bits
-  // (whole quads take this together: the merged list is the quad's).
+  // (whole quads take this together: the merged list is the quad's).  The
+  // picks with a higher high part keep their places; the class fills the
+  // KR - above positions below them, most often just the last one, for
+  // which one max per logit does.
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < KR; ++j) above += (L[j] >> idbits) > hmin;
   if (__builtin_amdgcn_ballot_w64(bnd)) {
-    if (bnd) {
-      int above = 0;  // picks with a higher high part keep their places
-#pragma unroll
-      for (int j = 0; j < KR; ++j) above += (L[j] >> idbits) > hmin;
+    const bool one = !__builtin_amdgcn_ballot_w64(bnd && above + 1 < KR);
+    if (bnd && one) {
+      uint32_t C[1];
+      if (E <= kChunkCols)
+        class_pass<1, true>(C, v, a, t, sub, vec4, hmin, idbits, idmask);
+      else
+        class_pass<1, false>(C, v, a, t, sub, vec4, hmin, idbits, idmask);
+      if (C[0] != 0u) id[KR - 1] = (int)(idmask - (C[0] & idmask));
+    } else if (bnd) {
       uint32_t C[KR];
-#pragma unroll
-      for (int j = 0; j < KR; ++j) C[j] = 0u;
-      if (E <= kChunkCols) {  // the row is still in registers
-#pragma unroll
-        for (int i = 0; i < kLaneCols; ++i)
-          list_insert<KR>(C, class_key(v[i], lane_col(0, sub, i), E, hmin, idbits, idmask));
-      } else {
-        for (int c0 = 0; c0 < E; c0 += kChunkCols) {
-#pragma unroll 1
-          for (int g = 0; g < kLaneCols / 16; ++g) {
-            float w[16];
-            load_group(w, a, t, c0, g, sub, vec4);
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-              list_insert<KR>(C, class_key(w[u], lane_col(c0, sub, 16 * g + u), E, hmin, idbits,
-                                           idmask));
-          }
-        }
-      }
-      list_merge<KR, kDppQuadXor1>(C);
-      list_merge<KR, kDppQuadXor2>(C);
+      if (E <= kChunkCols)
+        class_pass<KR, true>(C, v, a, t, sub, vec4, hmin, idbits, idmask);
+      else
+        class_pass<KR, false>(C, v, a, t, sub, vec4, hmin, idbits, idmask);
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
         // position j takes class entry j - above (compile-time j, runtime above)
@@ -280,48 +338,34 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
     pid[i] = e;
     pv[i] = (active && j < KR) ? a.logits[t * E + e] : 0.0f;
   }
-  // Picks that share a high part: order them by (value desc, id asc).
-  if (__builtin_amdgcn_ballot_w64(inner || bnd)) {
-    if (inner || bnd) {
-      uint32_t sk[KR];
-      int si[KR];
+  // Picks that share a high part (or came from the boundary class): their set
+  // is right, their order is by (value desc, id asc) on the exact values.
+  // Each lane ranks its own picks against the quad's KR picks and writes them
+  // at that rank; without such ties the rank of pick j is j.
+  int prank[NP];
 #pragma unroll
-      for (int j = 0; j < KR; ++j) {
-        sk[j] = 0u;
-        si[j] = 0x7FFFFFFF;
-      }
+  for (int i = 0; i < NP; ++i) prank[i] = sub + kSub * i;
+  const bool ties = __builtin_amdgcn_ballot_w64(inner || bnd) != 0;  // wave-uniform
+  float m = __uint_as_float(dpp<quad_bcast(0)>(__float_as_uint(pv[0])));  // pick 0: the max
+  if (ties) {
+    uint32_t xk[KR];
+    int xe[KR];
 #pragma unroll
-      for (int j = 0; j < KR; ++j) {  // gather pick j from quad lane j % 4, then insert
-        const uint32_t k = quad_get(okey(pv[j / kSub]), j % kSub);
-        const int e = (int)quad_get((uint32_t)pid[j / kSub], j % kSub);
+    for (int q = 0; q < KR; ++q) {
+      xk[q] = quad_get(okey(pv[q / kSub]), q % kSub);
+      xe[q] = (int)quad_get((uint32_t)pid[q / kSub], q % kSub);
+    }
+    uint32_t top = xk[0];
 #pragma unroll
-        for (int s = KR - 1; s > 0; --s) {  // exact insertion, bottom up
-          const bool take = k > sk[s] || (k == sk[s] && e < si[s]);
-          const bool shift = k > sk[s - 1] || (k == sk[s - 1] && e < si[s - 1]);
-          const uint32_t nk = shift ? sk[s - 1] : k;
-          const int ni = shift ? si[s - 1] : e;
-          sk[s] = take ? nk : sk[s];
-          si[s] = take ? ni : si[s];
-        }
-        const bool take0 = k > sk[0] || (k == sk[0] && e < si[0]);
-        sk[0] = take0 ? k : sk[0];
-        si[0] = take0 ? e : si[0];
-      }
+    for (int q = 1; q < KR; ++q) top = max(top, xk[q]);
+    m = okey_float(top);
 #pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        uint32_t k = 0u;
-        int e = 0;
+    for (int i = 0; i < NP; ++i) {
+      const uint32_t k = okey(pv[i]);
+      int r = 0;
 #pragma unroll
-        for (int q = 0; q < kSub; ++q)
-          if (kSub * i + q < KR && sub == q) {
-            k = sk[kSub * i + q];
-            e = si[kSub * i + q];
-          }
-        if (sub + kSub * i < KR) {
-          pid[i] = e;
-          pv[i] = okey_float(k);
-        }
-      }
+      for (int q = 0; q < KR; ++q) r += (xk[q] > k || (xk[q] == k && xe[q] < pid[i])) ? 1 : 0;
+      if (sub + kSub * i < KR) prank[i] = r;
     }
   }
 
@@ -330,7 +374,6 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
   if (a.score_fn == MOEDC_SCORE_SOFTMAX) {
     // Z = sum over all logits of exp(l - max), per lane in column order,
     // then lanes 0..3 in order.
-    const float m = __uint_as_float(dpp<quad_bcast(0)>(__float_as_uint(pv[0])));
     float z = 0.0f;
     if (active) {
       if (E <= kChunkCols) {
@@ -362,9 +405,20 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
 #pragma unroll
     for (int i = 0; i < NP; ++i) s[i] = 1.0f / (1.0f + expf(-pv[i]));
     float S = 0.0f;
+    if (ties) {
+      // in rank order: through the token's row of sorted_s (one wave's own
+      // lanes write and then read it)
 #pragma unroll
-    for (int j = 0; j < KR; ++j)
-      S += __uint_as_float(quad_get(__float_as_uint(s[j / kSub]), j % kSub));
+      for (int i = 0; i < NP; ++i)
+        if (sub + kSub * i < KR) sorted_s[r][prank[i]] = s[i];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < KR; ++q) S += sorted_s[r][q];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KR; ++j)
+        S += __uint_as_float(quad_get(__float_as_uint(s[j / kSub]), j % kSub));
+    }
 #pragma unroll
     for (int i = 0; i < NP; ++i) w[i] = s[i] / S;
   }
@@ -382,8 +436,8 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
       w[i] = 1.0f;
     }
     if (active && j < KT) {
-      a.topk_ids[t * KT + j] = pk[i];
-      a.topk_w[t * KT + j] = w[i];
+      a.topk_ids[t * KT + prank[i]] = pk[i];
+      a.topk_w[t * KT + prank[i]] = w[i];
       atomicOr(&tokmask[pk[i]], 1ull << r);
     }
   }
@@ -394,7 +448,7 @@ __global__ __launch_bounds__(256) void route_topk(RouteArgs a, int idbits, int n
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int j = sub + kSub * i;
-    if (active && j < KT) a.slots[t * KT + j] = __popcll(tokmask[pk[i]] & below);
+    if (active && j < KT) a.slots[t * KT + prank[i]] = __popcll(tokmask[pk[i]] & below);
   }
   for (int p = tid; p < P; p += 256)
     a.block_counts[(int64_t)p * nblk + blk] = __popcll(tokmask[p]);

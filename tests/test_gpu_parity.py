@@ -89,6 +89,65 @@ def test_route_ties_signed_zeros_and_degenerate_rows(score_fn, T):
     assert got["dropped"] == 30
 
 
+def _near_tie_rows(T, E, K, seed):
+    """Rows of E logits where picks share the packed key's high part: values
+    that differ only in the low 8 bits of their order key (a few ulps apart),
+    exactly equal values at several ids, and +-0 at the boundary.  Each row
+    draws one case: 0 all K picks a few ulps apart; 1 the last pick decided
+    among 3 near-equal values; 2 the last 4 picks decided among 6; 3 equal
+    values at several ids across the boundary; 4 +0 and -0 across the
+    boundary; 5 plain normal logits."""
+    rng = np.random.default_rng(seed)
+    lg = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    base = np.float32(2.0).view(np.uint32)
+    case = rng.integers(0, 6, T)
+    for t in range(T):
+        cols = rng.permutation(E)
+        c = case[t]
+        if c == 0:
+            d = rng.choice(256, K + 2, replace=False)
+            lg[t, cols[:K + 2]] = (base + d).astype(np.uint32).view(np.float32)
+        elif c in (1, 2):
+            big = K - 1 if c == 1 else K - 4
+            lg[t, cols[:big]] = 3.0 + np.arange(big, dtype=np.float32)
+            n = 3 if c == 1 else 6
+            d = rng.choice(256, n, replace=False)
+            lg[t, cols[big:big + n]] = (base + d).astype(np.uint32).view(np.float32)
+        elif c == 3:
+            lg[t, cols[:K - 2]] = 3.0 + np.arange(K - 2, dtype=np.float32)
+            lg[t, cols[K - 2:K + 3]] = 2.0
+        elif c == 4:
+            lg[t] = -np.abs(lg[t]) - 1.0
+            lg[t, cols[:K - 3]] = 1.0 + np.arange(K - 3, dtype=np.float32)
+            lg[t, cols[K - 3:K + 3:2]] = 0.0
+            lg[t, cols[K - 2:K + 3:2]] = -0.0
+    return lg
+
+
+@pytest.mark.parametrize("T", [700, 300])
+@pytest.mark.parametrize("score_fn", [W.SCORE_SOFTMAX, W.SCORE_SIGMOID_NORM])
+def test_route_near_ties_on_256_expert_rows(score_fn, T):
+    """Rows of 256 logits (the one-chunk rows of the large-batch route) with
+    picks whose packed keys tie: the exact order is (value desc, id asc),
+    and the sigmoid gates are normalised by the sum in that order."""
+    E, K = 256, 8
+    logits = _near_tie_rows(T, E, K, 31 + T)
+    wl = W.Workload("near-ties", "", T, 128, E, E, K, 0, score_fn,
+                    np.full(E, T, np.int32), None, 0, "normal")
+    want = oracle.route(oracle.Cfg.from_workload(wl), logits)
+    log(f"[case] near ties E=256 T={T} score_fn={score_fn}")
+    compare_route(wl, gpu_route(M.Plan.from_workload(wl), wl, logits)[0], want)
+    # with a shared expert and a replica table on the same rows
+    P = E + 17
+    rep = np.full((E, 2), -1, np.int32)
+    rep[:, 0] = np.arange(E)
+    rep[:16, 1] = E + np.arange(16)
+    wl2 = W.Workload("near-ties-rep", "", T, 128, E, P, K, 1, score_fn,
+                     np.full(P, T, np.int32), rep, 0, "normal")
+    want = oracle.route(oracle.Cfg.from_workload(wl2), logits)
+    compare_route(wl2, gpu_route(M.Plan.from_workload(wl2), wl2, logits)[0], want)
+
+
 @pytest.mark.parametrize("T", [1, 77, 256, 300])
 def test_route_widest_config(T):
     """1024 experts (16 logits per lane in the small-batch kernel), 15 routed
