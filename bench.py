@@ -381,7 +381,7 @@ def run(args):
             progress(f"{name}: {sub['ms_per_step']:.4f} ms per step")
             del sst
             torch.cuda.empty_cache()
-    if args.workload == "global" and not args.no_expert:
+    if args.workload == "global" and not args.no_expert and not args.no_lpt:
         res["expert_lpt"] = expert_lpt()
         progress("expert_lpt")
         torch.cuda.empty_cache()
@@ -1016,6 +1016,7 @@ def main():
     ap.add_argument("--no-placement", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--no-lpt", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=30720)
     ap.add_argument("--calib-copy", action="store_true")
