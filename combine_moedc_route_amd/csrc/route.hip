@@ -45,8 +45,8 @@
 // K2 route_scan: a wave per expert: exclusive scan of its row of block
 //    counts (in place) and the expert's total, counts[p].
 // K3 route_slots: a thread per entry: slot = base + block prefix +
-//    block-local rank, or -1 past capacity; the last workgroup scans counts
-//    into offsets through LDS and sums the drops.
+//    block-local rank, or -1 past capacity; workgroup 0 scans counts into
+//    offsets through LDS and sums the drops.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -465,36 +465,58 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 // One wave per physical expert: its row of block counts -> exclusive block
-// prefixes (in place) and the expert's total.
+// prefixes (in place) and the expert's total.  Lane l takes 8 consecutive
+// blocks (two 16-byte loads when the row allows), sums them serially, and
+// one wave scan of the lane totals gives every block's prefix.
 __global__ __launch_bounds__(256) void route_scan(int32_t *bc, int32_t *counts, int nblk, int P) {
   const int p = blockIdx.x * 4 + uniform(threadIdx.x >> 6);
   if (p >= P) return;
   const int l = lane_id();
   int32_t *row = bc + (int64_t)p * nblk;
+  const bool vec = (nblk & 3) == 0;  // rows 16-byte aligned (the workspace base is)
   int carry = 0;
   for (int b0 = 0; b0 < nblk; b0 += 512) {
+    const int b = b0 + 8 * l;
     int v[8];
+    if (vec && b + 8 <= nblk) {
+      const int4 x = *reinterpret_cast<const int4 *>(row + b);
+      const int4 y = *reinterpret_cast<const int4 *>(row + b + 4);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b + u < nblk ? row[b + u] : 0;
+    }
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+    const int incl = wave_inclusive_scan(sum);
+    int run = carry + incl - sum;  // blocks before b
+    int e[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int b = b0 + 64 * u + l;
-      v[u] = b < nblk ? row[b] : 0;
+      e[u] = run;
+      run += v[u];
     }
+    if (vec && b + 8 <= nblk) {
+      *reinterpret_cast<int4 *>(row + b) = make_int4(e[0], e[1], e[2], e[3]);
+      *reinterpret_cast<int4 *>(row + b + 4) = make_int4(e[4], e[5], e[6], e[7]);
+    } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + 64 * u + l;
-      const int incl = wave_inclusive_scan(v[u]);
-      if (b < nblk) row[b] = carry + incl - v[u];
-      carry += __shfl(incl, 63);
+      for (int u = 0; u < 8; ++u)
+        if (b + u < nblk) row[b + u] = e[u];
     }
+    carry += __shfl(incl, 63);
   }
   if (l == 0) counts[p] = carry;
 }
 
-// Entries -> slots; the last workgroup also scans counts into offsets and
-// counts the drops (LDS-staged block scan).
+// Entries -> slots; workgroup 0 also scans counts into offsets and counts
+// the drops (LDS-staged block scan).  It is dispatched first, so that
+// small serial job runs beside the entries instead of after them.
 __global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries, int nblk) {
   const int tid = threadIdx.x;
-  if (blockIdx.x == gridDim.x - 1) {
+  if (blockIdx.x == 0) {
     __shared__ int wave_tot[4];
     __shared__ int wave_drop[4];
     const int P = a.P;
@@ -529,7 +551,7 @@ __global__ __launch_bounds__(256) void route_slots(RouteArgs a, int64_t entries,
     if (tid == 0) a.dropped[0] = wave_drop[0] + wave_drop[1] + wave_drop[2] + wave_drop[3];
     return;
   }
-  const int64_t i = (int64_t)blockIdx.x * 256 + tid;
+  const int64_t i = (int64_t)(blockIdx.x - 1) * 256 + tid;
   if (i >= entries) return;
   const int64_t t = i / a.K;
   const int p = a.topk_ids[i];
