@@ -820,6 +820,91 @@ def overlap(rounds=20):
     return res
 
 
+def dispatch_trace(workload="global", sample_us=0.5):
+    """One moedc_dispatch of `workload` run by the trace build
+    (libmoedc_trace.so, per-wave phase stamps on the 100 MHz constant
+    clock): per-phase durations over all waves, and per CU, at every
+    `sample_us` of the launch, how many of its resident waves are loading
+    (start -> chunk loaded), quantizing (-> quantized) or storing (-> stores
+    complete) -- whether the load -> quantize -> write pipeline of the
+    token stream overlaps on each CU."""
+    import numpy as np
+    import torch
+
+    from combine_moedc_route_amd import build as B
+    from combine_moedc_route_amd import moedc as M
+    from combine_moedc_route_amd import workloads as W
+    import ctypes as C
+    wl = W.get(workload)
+    T, H = wl.tokens, wl.hidden
+    nw = -(-H // 512)
+    prev = M._lib
+    M._lib = M.load_library(B.TRACE_LIB)
+    try:
+        L = M._lib
+        L.moedc_trace_set.argtypes = [C.c_void_p, C.c_int64]
+        L.moedc_trace_set.restype = C.c_int32
+        plan = M.Plan.from_workload(wl)
+        b = plan.alloc("cuda:0")
+        x, logits = W.make_inputs(wl)
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        del x
+        plan.route(torch.from_numpy(logits).cuda(), b["topk_ids"], b["topk_w"], b["counts"],
+                   b["offsets"], b["slots"], b["dropped"], b["workspace"])
+        for _ in range(3):
+            plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+        tr = torch.zeros((T * nw, 8), dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
+        if L.moedc_trace_set(tr.data_ptr(), tr.numel() * 8):
+            raise RuntimeError("moedc_trace_set failed")
+        plan.dispatch(xd, b["slots"], b["dispatch_buf"])
+        torch.cuda.synchronize()
+        L.moedc_trace_set(None, 0)
+        rec = tr.cpu().numpy().view(np.uint64)
+        del plan, b, xd, tr
+        torch.cuda.empty_cache()
+    finally:
+        M._lib = prev
+    tok, wave = (rec[:, 0] >> np.uint64(32)).astype(np.int64), (rec[:, 0] & np.uint64(0xFFFF)).astype(np.int64)
+    idx = np.arange(T * nw)
+    written = bool(np.array_equal(tok * nw + wave, idx) and (rec[:, 2] > 0).all())
+    ts = rec[:, 2:].astype(np.int64)
+    ts = (ts - ts[:, 0].min()) * 1e-2  # us (10 ns ticks)
+    monotone = bool((np.diff(ts, axis=1) >= 0).all())
+    hw = rec[:, 1]
+    cu = ((hw >> np.uint64(32)) << np.uint64(8)) | ((hw >> np.uint64(8)) & np.uint64(0xFF))
+    names = ["load", "scales", "quantize", "store issue", "store complete"]
+    d = np.diff(ts, axis=1)
+    phases = {n: {"median_us": float(np.median(d[:, k])), "p90_us": float(np.percentile(d[:, k], 90)),
+                  "max_us": float(d[:, k].max())} for k, n in enumerate(names)}
+    span = float(ts[:, 5].max())
+    grid = np.arange(0.0, span, sample_us)
+    ucu, inv = np.unique(cu, return_inverse=True)
+    # per (CU, sample): waves in each phase
+    counts = np.zeros((3, len(ucu), len(grid)), np.int32)
+    bounds = [(0, 1), (1, 3), (3, 5)]  # load, quantize (scales + quantize), store
+    for k, (lo, hi) in enumerate(bounds):
+        a = np.searchsorted(grid, ts[:, lo], side="left")
+        z = np.searchsorted(grid, ts[:, hi], side="left")
+        diff = np.zeros((len(ucu), len(grid) + 1), np.int32)
+        np.add.at(diff, (inv, a), 1)
+        np.add.at(diff, (inv, z), -1)
+        counts[k] = np.cumsum(diff, axis=1)[:, :-1]
+    busy = counts.sum(0) > 0
+    both = (counts[0] > 0) & (counts[2] > 0)
+    three = (counts[0] > 0) & (counts[1] > 0) & (counts[2] > 0)
+    return {"workload": f"{workload}: {wl.description}", "waves": int(T * nw), "cus": int(len(ucu)),
+            "records_complete": written, "stamps_monotone": monotone,
+            "span_us": span, "phase_us": phases,
+            "resident_waves_per_cu_mean": float(counts.sum(0)[busy].mean()),
+            "frac_busy_cu_samples_loading_and_storing": float(both[busy].mean()),
+            "frac_busy_cu_samples_all_three_phases": float(three[busy].mean()),
+            "sample_us": sample_us,
+            "what": "per CU and time sample: waves between start and chunk loaded (loading), "
+                    "chunk loaded and quantized (quantizing), quantized and stores complete "
+                    "(storing)"}
+
+
 def placement(workers=8, redundant=32, max_replicas=8):
     """Load balancing on the skewed workload (Zipf(1.1) popularity over 256
     experts, top-8, 30720 tokens): per-expert loads from the device route,
@@ -1018,6 +1103,7 @@ def main():
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--no-lpt", action="store_true")
     ap.add_argument("--decode-only", action="store_true")
+    ap.add_argument("--dispatch-trace", metavar="WORKLOAD")
     ap.add_argument("--cpu-tokens", type=int, default=30720)
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--calib-bytes", type=int, default=4 << 30)
@@ -1039,6 +1125,9 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy(args)
+        return
+    if args.dispatch_trace:
+        print(json.dumps(dispatch_trace(args.dispatch_trace)), flush=True)
         return
     if args.decode_only:
         res = decode_latency()

@@ -16,6 +16,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoedc.so")
 # Measurement kernels for the benchmark's bandwidth ceilings (not the MoE path).
 CEILING_LIB = os.path.join(HERE, "libmoedc_ceiling.so")
+# The same library with dispatch's per-wave phase stamps (MOEDC_TRACE).
+TRACE_LIB = os.path.join(HERE, "libmoedc_trace.so")
 SOURCES = ["route.hip", "dispatch.hip", "fused.hip", "combine.hip", "stub.hip",
            "expert_gemm.hip", "noalloc.hip", "host.cpp", "planning.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,10 +31,11 @@ CFLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, verbose, defines=(), tag=""):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *["-D" + d for d in defines], *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,12 +54,16 @@ def _link(objs, lib, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + ["ceiling.hip"]
-    jobs = min(len(srcs), os.cpu_count() or 4, 8)
+    jobs_in = [(s, (), "") for s in SOURCES + ["ceiling.hip"]]
+    jobs_in.append(("dispatch.hip", ("MOEDC_TRACE",), "_trace"))
+    jobs = min(len(jobs_in), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
-    _link([objs[s] for s in SOURCES], LIB, verbose)
-    _link([objs["ceiling.hip"]], CEILING_LIB, verbose)
+        built = list(ex.map(lambda j: _compile(j[0], verbose, j[1], j[2]), jobs_in))
+    objs = {(s, tag): o for (s, _, tag), o in zip(jobs_in, built)}
+    _link([objs[(s, "")] for s in SOURCES], LIB, verbose)
+    _link([objs[("ceiling.hip", "")]], CEILING_LIB, verbose)
+    _link([objs[(s, "_trace" if s == "dispatch.hip" else "")] for s in SOURCES], TRACE_LIB,
+          verbose)
     return LIB
 
 

@@ -31,6 +31,16 @@
 // wave per (token, chunk) in 4-wave workgroups instead, with each chunk's
 // wave storing its own groups' scales: as fast at 16 tokens, 0.5 us faster
 // for one.  The bytes written are the same.
+//
+// Trace build (compiled with MOEDC_TRACE into libmoedc_trace.so only; see
+// include/moedc_trace.h): every wave of dispatch_token_block stamps the
+// 100 MHz constant clock at its phase boundaries -- start, chunk loaded,
+// scales known, quantized, stores issued, stores complete -- and writes
+// them with its hardware placement into a caller buffer, so that the
+// token-level load -> quantize -> write pipeline, which this kernel gets
+// from many resident waves per CU at different phases, can be seen.  The
+// analog of the per-core phase probes of "StrataCL 深度技术分析", section
+// on the NPU-side profiler.  The bytes dispatch writes are the same.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -38,6 +48,11 @@
 #include "quant.hpp"
 
 namespace moedc {
+
+#ifdef MOEDC_TRACE
+__device__ uint64_t *g_trace = nullptr;  // 8 words per (token, wave) record
+__device__ int64_t g_trace_records = 0;
+#endif
 
 namespace {
 
@@ -89,9 +104,18 @@ __global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
     const int s = a.slots[(int64_t)t * a.K + threadIdx.x];
     slot_of[threadIdx.x] = (uint32_t)s < (uint32_t)a.total_slots ? s : -1;
   }
+#ifdef MOEDC_TRACE
+  // The empty asm statements pin each stamp after the value it follows.
+  uint64_t ts[6];
+  ts[0] = wall_clock64();
+#endif
   const uint4 v = e < H ? reinterpret_cast<const uint4 *>(a.x + (int64_t)t * H)[wave * 64 + lane]
                         : make_uint4(0, 0, 0, 0);
   uint32_t m = row16_max_u32(absmax8(v));
+#ifdef MOEDC_TRACE
+  asm volatile("" : : "v"(m) : "memory");
+  ts[1] = wall_clock64();
+#endif
   float sc, word;
   bool has_word;
   if (PER_TOKEN) {
@@ -113,7 +137,15 @@ __global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
     has_word = wave == (int)(blockDim.x >> 6) - 1 && lane < scale_words(a.G);
     word = lane < a.G ? __uint_as_float(wave_max[lane]) : 0.0f;
   }
+#ifdef MOEDC_TRACE
+  asm volatile("" : : "v"(sc) : "memory");
+  ts[2] = wall_clock64();
+#endif
   const uint2 q = quant8(v, sc);
+#ifdef MOEDC_TRACE
+  asm volatile("" : : "v"(q.x), "v"(q.y) : "memory");
+  ts[3] = wall_clock64();
+#endif
   for (int k = 0; k < a.K; ++k) {
     const int slot = slot_of[k];
     if (slot < 0) continue;  // dropped, or outside the buffer
@@ -124,9 +156,34 @@ __global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
     }
     if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
+#ifdef MOEDC_TRACE
+  ts[4] = wall_clock64();
+  __builtin_amdgcn_s_waitcnt(0);  // the stores have completed
+  ts[5] = wall_clock64();
+  // Record: [token << 32 | wave, XCC_ID << 32 | HW_ID, stamps 0..5].
+  const int64_t rec = (int64_t)t * (int64_t)(blockDim.x >> 6) + wave;
+  if (g_trace != nullptr && lane < 8 && rec < g_trace_records) {
+    const uint64_t hw = ((uint64_t)__builtin_amdgcn_s_getreg((15 << 11) | 20) << 32) |
+                        (uint64_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);
+    uint64_t w = lane == 0 ? (((uint64_t)(uint32_t)t << 32) | (uint32_t)wave) : hw;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) w = lane == k + 2 ? ts[k] : w;
+    g_trace[8 * rec + lane] = w;
+  }
+#endif
 }
 
 }  // namespace
+
+#ifdef MOEDC_TRACE
+extern "C" int32_t moedc_trace_set(void *buf, int64_t bytes) {
+  uint64_t *ptr = static_cast<uint64_t *>(buf);
+  const int64_t n = (buf != nullptr && bytes > 0) ? bytes / 64 : 0;
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_trace), &ptr, sizeof(ptr));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_trace_records), &n, sizeof(n));
+  return (int32_t)e;
+}
+#endif
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

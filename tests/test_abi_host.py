@@ -40,6 +40,19 @@ def test_ceiling_library_exports_every_declared_symbol():
         assert getattr(L, n) is not None
 
 
+def test_trace_library_exports_the_library_and_its_trace_call():
+    """libmoedc_trace.so (dispatch with per-wave phase stamps) exports every
+    symbol of include/moedc.h and moedc_trace_set (include/moedc_trace.h);
+    libmoedc.so does not carry the trace call."""
+    from combine_moedc_route_amd import build as B
+    assert declared_functions(os.path.join(ROOT, "include", "moedc_trace.h")) == ["moedc_trace_set"]
+    T = C.CDLL(B.TRACE_LIB)
+    for n in declared_functions() + ["moedc_trace_set"]:
+        assert getattr(T, n) is not None
+    with pytest.raises(AttributeError):
+        getattr(M.lib(), "moedc_trace_set")
+
+
 def test_status_strings():
     for s in range(7):
         assert M.status_string(s)
