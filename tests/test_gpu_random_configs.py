@@ -1,7 +1,7 @@
 """Seeded random layer configurations through the whole C-ABI path.
 
 Each case draws a configuration (hidden size 128..8192, 128-value or
-per-token scales, 1..300 logical experts, 1..16 picks, an optional shared
+per-token scales, 1..300 logical experts (256 in a quarter of the cases), 1..16 picks, an optional shared
 expert, multi-copy replicas, capacities that may overflow, normal, uniform
 or tie-heavy logits, token counts on both sides of the small-batch switch)
 and checks against the oracle: route (integers exact, gates within the
@@ -31,7 +31,9 @@ def random_case(seed):
     H = int(rng.choice([128, 256, 640, 1152, 4096, 8192]))
     gs = H if rng.random() < 0.3 else 128
     shared = int(rng.random() < 0.3)
-    E = int(rng.integers(1, 301))
+    # a quarter of the cases use rows of exactly 256 logits (the large-batch
+    # route's one-chunk path)
+    E = 256 if rng.random() < 0.25 else int(rng.integers(1, 301))
     KR = int(rng.integers(1, min(E, 16 - shared) + 1))
     R = int(rng.choice([1, 1, 2, 3]))
     rep, extra = None, 0
