@@ -18,11 +18,11 @@
 //      = larger value, or the same high part and a lower id.  Each lane
 //      keeps its top KR + 1 keys sorted, one v_med3_u32 per list entry per
 //      logit (insertion is L[j] = med3(L[j-1], L[j], c), L[0] = max(L[0],
-//      c)), and the token's four lists merge through quad DPP.  The kernel
-//      is bound by VALU issue, so rows of exactly 256 logits (one chunk)
-//      take a path with unguarded loads (compute starts on the first while
-//      the rest are in flight) and 5 instructions of key building per logit
-//      besides the 9 of the insertion.
+//      c)), and the token's four lists merge through quad DPP.  Rows of
+//      exactly 256 logits (one chunk) take a path with unguarded loads
+//      (compute starts on the first while the rest are in flight) and 5
+//      instructions of key building per logit besides the 9 of the
+//      insertion; with it the scan overlaps the arrival of the logits.
 //    - Exactness.  Where the high parts (the key without the id bits) of
 //      the merged top KR + 1 strictly decrease, the first KR keys are the
 //      top KR logits by (value desc, id asc) in that order: every other
