@@ -865,6 +865,15 @@ def dispatch_trace(workload="global", sample_us=0.5):
         torch.cuda.empty_cache()
     finally:
         M._lib = prev
+    return {"workload": f"{workload}: {wl.description}",
+            **trace_summary(rec, T, nw, sample_us)}
+
+
+def trace_summary(rec, T, nw, sample_us=0.5):
+    """Decode dispatch trace records (uint64 [T * nw][8], the layout of
+    include/moedc_trace.h) into per-phase durations and the per-CU phase
+    overlap over the launch."""
+    import numpy as np
     tok, wave = (rec[:, 0] >> np.uint64(32)).astype(np.int64), (rec[:, 0] & np.uint64(0xFFFF)).astype(np.int64)
     idx = np.arange(T * nw)
     written = bool(np.array_equal(tok * nw + wave, idx) and (rec[:, 2] > 0).all())
@@ -893,7 +902,7 @@ def dispatch_trace(workload="global", sample_us=0.5):
     busy = counts.sum(0) > 0
     both = (counts[0] > 0) & (counts[2] > 0)
     three = (counts[0] > 0) & (counts[1] > 0) & (counts[2] > 0)
-    return {"workload": f"{workload}: {wl.description}", "waves": int(T * nw), "cus": int(len(ucu)),
+    return {"waves": int(T * nw), "cus": int(len(ucu)),
             "records_complete": written, "stamps_monotone": monotone,
             "span_us": span, "phase_us": phases,
             "resident_waves_per_cu_mean": float(counts.sum(0)[busy].mean()),

@@ -153,3 +153,38 @@ def test_summary_splits_a_kernel_launched_with_several_grid_sizes(tmp_path):
     assert "per launch shape" in text
     assert "     1     430.00     430.00     430.00   27525120   896" in text
     assert "     2       5.00       4.00       6.00      86016   896" in text
+
+
+def test_trace_summary_decodes_records_and_overlap():
+    """Synthetic dispatch trace records (include/moedc_trace.h layout): two
+    tokens of two waves on two CUs, times in 10 ns ticks."""
+    import numpy as np
+    T, nw = 2, 2
+    rec = np.zeros((T * nw, 8), np.uint64)
+    hw_a = (np.uint64(3) << np.uint64(32)) | np.uint64(0x0500)   # XCC 3, CU bits 0x05
+    hw_b = (np.uint64(1) << np.uint64(32)) | np.uint64(0x0A00)   # XCC 1, CU bits 0x0A
+    #         start loaded scales quant issued done   (ticks)
+    stamps = [[100, 200, 250, 260, 300, 400],   # token 0 wave 0, CU A
+              [350, 450, 470, 480, 520, 600],   # token 0 wave 1, CU A: loads while wave 0 stores
+              [100, 150, 160, 170, 180, 200],   # token 1 wave 0, CU B
+              [900, 950, 960, 970, 980, 1000]]  # token 1 wave 1, CU B
+    for i, st in enumerate(stamps):
+        t, w = divmod(i, nw)
+        rec[i, 0] = (np.uint64(t) << np.uint64(32)) | np.uint64(w)
+        rec[i, 1] = hw_a if i < 2 else hw_b
+        rec[i, 2:] = np.array(st, np.uint64)
+    r = bench.trace_summary(rec, T, nw, sample_us=0.1)
+    assert r["records_complete"] and r["stamps_monotone"]
+    assert r["waves"] == 4 and r["cus"] == 2
+    assert abs(r["span_us"] - 9.0) < 1e-9                        # (1000 - 100) ticks
+    assert abs(r["phase_us"]["load"]["median_us"] - 0.75) < 1e-9  # loads 1.0, 1.0, 0.5, 0.5 us
+    assert abs(r["phase_us"]["store complete"]["max_us"] - 1.0) < 1e-9
+    # CU A at 3.5-4.0 us: wave 1 loading, wave 0 storing -> some overlap, but not everywhere
+    assert 0 < r["frac_busy_cu_samples_loading_and_storing"] < 1
+    # a record missing (zero stamps) or out of order is reported
+    bad = rec.copy()
+    bad[3, 2:] = 0
+    assert not bench.trace_summary(bad, T, nw)["records_complete"]
+    bad = rec.copy()
+    bad[0, 4] = 150   # quantized before scales known
+    assert not bench.trace_summary(bad, T, nw)["stamps_monotone"]
