@@ -521,6 +521,7 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, xd, slots, iters=5):
     plan_pt.dispatch(xd, slots, dbuf)
     us_pt = timed(plan_pt, ws_pt)
     lib_us = library_int8_gemm(wl, counts, dbuf, Wd, plan.sizes.slot_stride, iters)
+    floor = mfma_floor(ops)
     del Wd
     torch.cuda.empty_cache()
     tops, tops_pt = ops / (us * 1e-6) / 1e12, ops / (us_pt * 1e-6) / 1e12
@@ -529,11 +530,40 @@ def expert_gemm(plan, wl, counts, dbuf, cbuf, ws, xd, slots, iters=5):
                          "unit": "TOP/s (int8)", "frac": tops / INT8_PEAK_TOPS,
                          "traffic": measured_traffic("expert_gemm")},
             "weight_GBps": P * H * H / (us * 1e-6) / 1e9,
-            "per_token_scales": {"us": us_pt, "TOPs": tops_pt, "frac": tops_pt / INT8_PEAK_TOPS},
+            "per_token_scales": {"us": us_pt, "TOPs": tops_pt, "frac": tops_pt / INT8_PEAK_TOPS,
+                                 "frac_of_compute_floor": floor["per_token_us"] / us_pt},
+            "compute_floor": floor,
+            "frac_of_compute_floor": floor["groups_us"] / us,
             "library_int8_gemm": {
                 "what": "torch._int_mm (hipBLASLt) once per expert on the same rows and weights, "
                         "int32 out, no scales: context, not part of the path",
                 "us": lib_us, "frac": ops / (lib_us * 1e-6) / 1e12 / INT8_PEAK_TOPS}}
+
+
+def mfma_floor(ops, iters=3):
+    """The expert layer's compute floor on this part (libmoedc_ceiling's
+    MFMA kernel): the layer's int8 MACs as v_mfma_i32_16x16x64_i8 from
+    registers, two waves per SIMD, no memory traffic; with the 128-input
+    groups' fold after every 32 MFMAs per wave, and without (one scale per
+    token)."""
+    import torch
+    L = _ceiling_lib()
+    cs = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n = int(ops // (2 * 16 * 16 * 64))
+
+    def run(fold):
+        rc = L.moedc_ceiling_mfma(n, fold, sink.data_ptr(), cs)
+        if rc:
+            raise RuntimeError(f"ceiling kernel failed: hip error {rc}")
+
+    res = {"mfma": n, "what": "the layer's MACs as 16x16x64 int8 MFMAs from registers, "
+                              "2 waves per SIMD, no memory; groups: plus the per-group fold"}
+    for key, fold in (("per_token_us", 0), ("groups_us", 1)):
+        res[key] = _time_us(lambda: run(fold), iters=iters, warm=1)
+    res["per_token_frac_of_int8_peak"] = ops / (res["per_token_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS
+    res["groups_frac_of_int8_peak"] = ops / (res["groups_us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS
+    return res
 
 
 def library_int8_gemm(wl, counts, dbuf, Wd, slot_stride, iters):
@@ -577,7 +607,8 @@ def _ceiling_lib():
     L.moedc_ceiling_copy.argtypes = [P, P, i64, P]
     L.moedc_ceiling_scatter.argtypes = [P, i32, i32, P, i64, i32, P]
     L.moedc_ceiling_gather.argtypes = [P, P, i32, i32, i64, i32, P, P]
-    for f in ("read", "write", "copy", "scatter", "gather"):
+    L.moedc_ceiling_mfma.argtypes = [i64, i32, P, P]
+    for f in ("read", "write", "copy", "scatter", "gather", "mfma"):
         getattr(L, "moedc_ceiling_" + f).restype = i32
     return L
 

@@ -1,7 +1,9 @@
-// ceiling.hip -- measurement kernels for the memory system's attainable
-// bandwidth (libmoedc_ceiling.so): plain streams, and dispatch's store and
-// combine's load patterns with their arithmetic taken out.  Not part of the
-// MoE path; the benchmark reads dispatch and combine against these.
+// ceiling.hip -- measurement kernels (libmoedc_ceiling.so): the memory
+// system's attainable bandwidth for plain streams and for dispatch's store
+// and combine's load patterns with their arithmetic taken out, and the
+// compute floor of the expert layer's instruction mix with its memory
+// traffic taken out.  Not part of the MoE path; the benchmark reads
+// dispatch, combine and the expert layer against these.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,6 +93,53 @@ __global__ __launch_bounds__(1024) void gather_kernel(const uint8_t *rows, const
   if (off < row_bytes) st_nt(acc, reinterpret_cast<u32x4 *>(out + (int64_t)t * row_bytes + off));
 }
 
+// The expert layer's per-wave instruction mix without memory: per K step,
+// 2 x 16 v_mfma_i32_16x16x64_i8 on 16 accumulators from register operands
+// and, with FOLD, the fold of the 64 int32 sums into fp32 (a convert and an
+// FMA each, the first MFMA of the step on a zero accumulator) -- the
+// 128-input-group kernel's step; without FOLD the sums carry on (the
+// one-scale-per-token kernel).  512-thread workgroups: two waves per SIMD.
+typedef int v4i __attribute__((ext_vector_type(4)));
+template <bool FOLD>
+__global__ __launch_bounds__(512) void mfma_kernel(int steps, float s, int *sink) {
+  // 4 A and 4 B fragments, 16 accumulators (the layer's 4 x 4 blocking).
+  v4i av[4], bv[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    av[f] = v4i{(int)threadIdx.x + f, 0x01020304 * (f + 1), 0x7F7F7F7F ^ f, (int)blockIdx.x};
+    bv[f] = v4i{0x05060708 + f, (int)threadIdx.x * (3 + f), 0x11223344, 0x7F00FF01 - f};
+  }
+  v4i acc[16];
+  float accf[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[i] = v4i{i, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) accf[i][q] = 0.0f;
+  }
+  for (int g = 0; g < steps; ++g) {
+    av[0].x += g;  // operands that change every step: nothing is loop-invariant
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            av[i >> 2], bv[i & 3], (FOLD && kk == 0) ? v4i{0, 0, 0, 0} : acc[i], 0, 0, 0);
+    if (FOLD) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) accf[i][q] = __builtin_fmaf(s, (float)acc[i][q], accf[i][q]);
+    }
+  }
+  int r = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r += FOLD ? (int)accf[i][q] : acc[i][q];
+  if (r == 0x5A5A5A5A) sink[0] = r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +180,17 @@ int32_t moedc_ceiling_gather(const void *rows, const int32_t *slots, int32_t T, 
   gather_kernel<<<(unsigned)((units + 15) / 16), 1024, 0, s>>>(
       static_cast<const uint8_t *>(rows), slots, T, K, row_stride, row_bytes,
       static_cast<uint8_t *>(out));
+  return (int32_t)hipGetLastError();
+}
+
+int32_t moedc_ceiling_mfma(int64_t mfma_total, int32_t fold, uint32_t *sink, hipStream_t s) {
+  // 256 workgroups x 8 waves, 32 MFMAs per wave and step.
+  const int64_t steps = mfma_total / (256 * 8 * 32);
+  if (steps <= 0 || steps > (1 << 30)) return (int32_t)hipErrorInvalidValue;
+  if (fold)
+    mfma_kernel<true><<<256, 512, 0, s>>>((int)steps, 1.0e-3f, reinterpret_cast<int *>(sink));
+  else
+    mfma_kernel<false><<<256, 512, 0, s>>>((int)steps, 1.0e-3f, reinterpret_cast<int *>(sink));
   return (int32_t)hipGetLastError();
 }
 

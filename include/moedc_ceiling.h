@@ -3,14 +3,15 @@
  * the MoE path: what one MI355X's memory system delivers for plain streams
  * and for the exact access patterns of dispatch and combine, so that their
  * achieved bandwidth can be read against a measured ceiling as well as the
- * 8 TB/s HBM peak.  The pages measure their operators the same way against
+ * 8 TB/s HBM peak, and the compute floor of the expert layer's instruction
+ * mix, read against the 5 POP/s int8 peak likewise.  The pages measure their operators the same way against
  * their fabric ("StrataCL 深度技术分析", section 4.1: bus bandwidth of
  * dispatch and combine).
  *
  * Every call enqueues one kernel on `stream` and returns the launch's
  * hipError_t (0 on success).  Device pointers are 16-byte aligned, byte
- * counts multiples of 16.  The kernels move data only: no arithmetic of the
- * method runs in them.
+ * counts multiples of 16.  No arithmetic of the method runs in them: the
+ * memory kernels move data only, the MFMA kernel computes on constants.
  */
 #ifndef MOEDC_CEILING_H
 #define MOEDC_CEILING_H
@@ -50,6 +51,15 @@ int32_t moedc_ceiling_scatter(const int32_t *slots, int32_t T, int32_t K, void *
  * expert outputs.  row_bytes: a multiple of 16, at most 16384. */
 int32_t moedc_ceiling_gather(const void *rows, const int32_t *slots, int32_t T, int32_t K,
                              int64_t row_stride, int32_t row_bytes, void *out, hipStream_t stream);
+
+/* The expert layer's compute floor: about mfma_total v_mfma_i32_16x16x64_i8
+ * (rounded down to whole steps of 32 per wave) issued from registers by 256
+ * workgroups of 8 waves (two per SIMD), with no memory traffic; with fold
+ * != 0 each wave also folds its 64 int32 sums into fp32 after every 32
+ * MFMAs (a convert and an FMA each), the per-group work of 128-input
+ * activation scales.  sink: device uint32 [1], written only if a fold of
+ * the results hits a value none produces. */
+int32_t moedc_ceiling_mfma(int64_t mfma_total, int32_t fold, uint32_t *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

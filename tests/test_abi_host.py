@@ -33,8 +33,8 @@ def test_ceiling_library_exports_every_declared_symbol():
     """libmoedc_ceiling.so (the benchmark's bandwidth-ceiling kernels) loads
     and exports what include/moedc_ceiling.h declares."""
     names = declared_functions(os.path.join(ROOT, "include", "moedc_ceiling.h"))
-    assert names == ["moedc_ceiling_copy", "moedc_ceiling_gather", "moedc_ceiling_read",
-                     "moedc_ceiling_scatter", "moedc_ceiling_write"]
+    assert names == ["moedc_ceiling_copy", "moedc_ceiling_gather", "moedc_ceiling_mfma",
+                     "moedc_ceiling_read", "moedc_ceiling_scatter", "moedc_ceiling_write"]
     L = C.CDLL(os.path.join(ROOT, "combine_moedc_route_amd", "libmoedc_ceiling.so"))
     for n in names:
         assert getattr(L, n) is not None
