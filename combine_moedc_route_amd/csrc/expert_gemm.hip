@@ -61,6 +61,7 @@ constexpr int BK = 128;   // inputs per K step
 // banks, and the tiles need no padding.
 __device__ __forceinline__ int swz(int r, int chunk) { return 16 * (chunk ^ (r & 7)); }
 constexpr int kThreads = 512;   // 8 waves: 2 token halves x 4 channel quarters
+constexpr int kDppRowHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7 - i within 8
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -147,11 +148,13 @@ __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
     }
   }
   if (tid >= 64) return;
-  // One wave, wave-uniform loop: loads and counts stay in scalar registers.
+  // One wave places the bands in that order.  Lane x < 8 holds XCD x's
+  // tiles and bands so far; the least-loaded XCD (ties to the lower one) is
+  // the minimum of (tiles << 3 | x) over lanes 0-7, three DPP steps.  Lane i
+  // remembers where band i of the current 64 went, and the 64 placements
+  // are stored together after the chunk.
   const int lane = tid;
-  int load[kXcds], cnt[kXcds];
-#pragma unroll
-  for (int x = 0; x < kXcds; ++x) load[x] = cnt[x] = 0;
+  int load_l = 0, cnt_l = 0;
   bool more = true;
   for (int base = 0; base < nb && more; base += 64) {
     // 64 bands at a time: each lane fetches one band's exact cost (the key
@@ -160,41 +163,40 @@ __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
     const int mine_k = 8191 - (int)(mine & 8191u);
     const int mine_cost = (mine >> 13) ? band_cost(a, mine_k) : 0;
     const int n = min(64, nb - base);
+    int my_x = -1, my_j = 0, my_pre = 0;
     for (int i = 0; i < n; ++i) {
       const int cost = __builtin_amdgcn_readlane(mine_cost, i);
       if (cost == 0) {  // the rest have no tiles
         more = false;
         break;
       }
-      const int k = __builtin_amdgcn_readlane(mine_k, i);
-      int bx = 0, bl = load[0];
-#pragma unroll
-      for (int x = 1; x < kXcds; ++x)
-        if (load[x] < bl) {
-          bl = load[x];
-          bx = x;
-        }
-      int j = 0;
-#pragma unroll
-      for (int x = 0; x < kXcds; ++x) j = x == bx ? cnt[x] : j;
-      if (lane == 0) {
-        a.band_list[bx * Jm + j] = k;
-        a.band_pre[bx * (Jm + 1) + j] = bl;
+      uint32_t key = lane < kXcds ? ((uint32_t)load_l << 3) | (uint32_t)lane : 0xFFFFFFFFu;
+      key = min(key, dpp<kDppQuadXor1>(key));
+      key = min(key, dpp<kDppQuadXor2>(key));
+      key = min(key, dpp<kDppRowHalfMirror>(key));  // lanes 0-3 with 4-7
+      const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)key);
+      const int bx = (int)(m & 7u);
+      const int j = __builtin_amdgcn_readlane(cnt_l, bx);
+      if (lane == i) {
+        my_x = bx;
+        my_j = j;
+        my_pre = (int)(m >> 3);
       }
-#pragma unroll
-      for (int x = 0; x < kXcds; ++x) {
-        load[x] += x == bx ? cost : 0;
-        cnt[x] += x == bx ? 1 : 0;
+      if (lane == bx) {
+        load_l += cost;
+        cnt_l += 1;
       }
+    }
+    if (my_x >= 0) {
+      a.band_list[my_x * Jm + my_j] = mine_k;
+      a.band_pre[my_x * (Jm + 1) + my_j] = my_pre;
     }
   }
-#pragma unroll
-  for (int x = 0; x < kXcds; ++x)
-    if (lane == x) {
-      a.band_pre[x * (Jm + 1) + cnt[x]] = load[x];
-      a.band_cnt[x] = cnt[x];
-      if (a.xcd_tiles) a.xcd_tiles[x] = load[x];
-    }
+  if (lane < kXcds) {
+    a.band_pre[lane * (Jm + 1) + cnt_l] = load_l;
+    a.band_cnt[lane] = cnt_l;
+    if (a.xcd_tiles) a.xcd_tiles[lane] = load_l;
+  }
 }
 
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
