@@ -114,7 +114,7 @@ def measured_traffic(kernel, workload="global"):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(tokens=30720, reps=3):
+def cpu_baseline(tokens=30720, reps=3, keep=None):
     """The oracle, single-threaded and pinned to one host core, on the same
     workload recipe (`tokens` tokens, seed and capacity as on the GPU when
     tokens = 30720).  Route, dispatch and combine are each timed `reps`
@@ -173,6 +173,8 @@ def cpu_baseline(tokens=30720, reps=3):
     except (OSError, StopIteration):
         pass
     sec = sum(med)
+    if keep is not None:  # the oracle's outputs, for the parity check of the timed GPU step
+        keep.update(route=r, dbuf=dbuf, y=y, slot_stride=sd)
     return {"value": tokens / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{tokens} tokens of the {wl.tokens}-token workload recipe "
                       f"(capacity {int(sub.capacity[0])}/expert), 1 core ({model}, core {core}); "
@@ -180,6 +182,46 @@ def cpu_baseline(tokens=30720, reps=3):
                       f"runs per step: route {1e3 * med[0]:.1f} ms, dispatch {1e3 * med[1]:.1f} ms, "
                       f"combine {1e3 * med[2]:.1f} ms (single thread, "
                       f"{sum(t_r) + sum(t_d) + sum(t_c):.1f} s timed in all)"}
+
+
+def gpu_snapshot(st):
+    """Host copies of what the last timed step left on the GPU: route
+    outputs, the dispatch buffer (both sets hold the same slots) and y."""
+    out = {k: st[k].cpu().numpy() for k in ("slots", "w")}
+    out.update({k: v.cpu().numpy() for k, v in st["route_out"].items()})
+    out["dbuf"] = st["sets"][0][0].cpu().numpy()
+    out["y"] = st["y"].cpu().numpy().view("uint16")
+    return out
+
+
+def parity(gpu, orc):
+    """The timed step's GPU outputs against the oracle on the same inputs:
+    route integers and INT8 slot bytes bit for bit, gates and BF16 outputs
+    as the largest difference in units in the last place."""
+    import numpy as np
+    r = orc["route"]
+    occ = r["slots"][r["slots"] >= 0]
+    sd = orc["slot_stride"]
+    H = gpu["y"].shape[1]
+    nbytes = H + 4 * (H // 128)
+    dg = gpu["dbuf"].reshape(-1, sd)
+    dispatch_exact = bool(np.array_equal(dg[occ, :nbytes], orc["dbuf"][occ, :nbytes]))
+    wg = gpu["w"].astype(np.float32).view(np.int32).astype(np.int64)
+    wo = r["topk_w"].astype(np.float32).view(np.int32).astype(np.int64)
+    yd = np.abs(gpu["y"].astype(np.int32) - orc["y"].astype(np.int32))
+    return {"route_ids_slots_counts_exact": bool(
+                np.array_equal(gpu["topk_ids"], r["topk_ids"]) and
+                np.array_equal(gpu["slots"], r["slots"]) and
+                np.array_equal(gpu["counts"], r["counts"]) and
+                np.array_equal(gpu["offsets"], r["offsets"]) and
+                int(gpu["dropped"][0]) == int(r["dropped"])),
+            "gates_max_ulp": int(np.abs(wg - wo).max()),
+            "dispatch_slot_bytes_exact": dispatch_exact,
+            "combine_max_bf16_ulp": int(yd.max()),
+            "combine_tokens_not_bit_identical": int((yd.max(axis=1) > 0).sum()),
+            "what": f"every token of the timed step ({gpu['y'].shape[0]}): route outputs, bytes "
+                    f"[0, {nbytes}) of all {len(occ)} occupied slots, y; against the oracle "
+                    "outputs of the cpu_baseline leg (same inputs)"}
 
 
 def measure_path(wl, steps, warmup, fmt_name="bf16"):
@@ -291,7 +333,8 @@ def measure_path(wl, steps, warmup, fmt_name="bf16"):
         "wall_s_timed": wall,
     }
     state = dict(plan=plan, wl=wl, counts=counts, sets=sets, ws=ws, xd=xd, slots=slots, w=w,
-                 y=y, fmt=fmt, ab=ab, cb=cb)
+                 y=y, fmt=fmt, ab=ab, cb=cb,
+                 route_out=dict(topk_ids=ids, counts=counts, offsets=offsets, dropped=dropped))
     return out, state
 
 
@@ -306,6 +349,10 @@ def run(args):
     torch.cuda.set_device(0)
     m, st = measure_path(wl, args.steps, args.warmup, args.combine_fmt)
     progress(f"{wl.name}: {m['ms_per_step']:.4f} ms per step")
+    # The timed step's outputs, for the parity check against the oracle
+    # (taken now: later legs reuse these buffers).
+    snap = (gpu_snapshot(st) if args.workload == "global" and args.cpu_tokens == wl.tokens
+            and args.combine_fmt == "bf16" and not args.no_cpu_baseline else None)
     fmt, ab, cb = st["fmt"], st["ab"], st["cb"]
     plan, sets, slots, w, y = st["plan"], st["sets"], st["slots"], st["w"], st["y"]
     # Dominant kernel: the one with the larger mean duration.
@@ -398,7 +445,12 @@ def run(args):
         res["placement"] = placement()
         progress("placement")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        orc = {} if snap is not None else None
+        res["cpu_baseline"] = cpu_baseline(args.cpu_tokens, keep=orc)
+        if snap is not None:
+            res["parity"] = parity(snap, orc)
+            progress(f"parity {res['parity']}")
+            del snap, orc
     print(json.dumps(res), flush=True)
 
 

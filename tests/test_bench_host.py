@@ -188,3 +188,36 @@ def test_trace_summary_decodes_records_and_overlap():
     bad = rec.copy()
     bad[0, 4] = 150   # quantized before scales known
     assert not bench.trace_summary(bad, T, nw)["stamps_monotone"]
+
+
+def test_parity_compares_route_slots_and_outputs():
+    """bench.parity on a small synthetic case: equal outputs report exact
+    and zero ulps; a changed slot byte, gate ulp or BF16 step is reported."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    T, K, H, S, sd = 6, 2, 256, 20, 512
+    slots = rng.choice(S, (T, K), replace=False).astype(np.int32)
+    slots[0, 1] = -1
+    r = {"topk_ids": rng.integers(0, 8, (T, K)).astype(np.int32), "slots": slots,
+         "counts": np.arange(8, dtype=np.int32), "offsets": np.arange(9, dtype=np.int32),
+         "dropped": 1, "topk_w": rng.random((T, K)).astype(np.float32)}
+    dbuf = rng.integers(0, 256, (S, sd)).astype(np.uint8)
+    y = rng.integers(0, 2 ** 16, (T, H)).astype(np.uint16)
+    orc = {"route": r, "dbuf": dbuf, "y": y, "slot_stride": sd}
+    gpu = {"topk_ids": r["topk_ids"].copy(), "slots": slots.copy(), "counts": r["counts"].copy(),
+           "offsets": r["offsets"].copy(), "dropped": np.array([1], np.int32),
+           "w": r["topk_w"].copy(), "dbuf": dbuf.reshape(-1).copy(), "y": y.copy()}
+    p = bench.parity(gpu, orc)
+    assert p["route_ids_slots_counts_exact"] and p["dispatch_slot_bytes_exact"]
+    assert p["gates_max_ulp"] == 0 and p["combine_max_bf16_ulp"] == 0
+    unused = np.setdiff1d(np.arange(S), slots[slots >= 0])[0]
+    gpu["dbuf"][unused * sd] ^= 1            # a byte outside every occupied slot: not compared
+    assert bench.parity(gpu, orc)["dispatch_slot_bytes_exact"]
+    gpu["dbuf"][slots[2, 0] * sd + 5] ^= 1   # a payload byte of an occupied slot
+    gpu["w"][1, 1] = np.nextafter(gpu["w"][1, 1], np.float32(2))
+    gpu["y"][3, 7] += 1
+    gpu["slots"][4, 0] = -1
+    p = bench.parity(gpu, orc)
+    assert not p["dispatch_slot_bytes_exact"] and not p["route_ids_slots_counts_exact"]
+    assert p["gates_max_ulp"] == 1 and p["combine_max_bf16_ulp"] == 1
+    assert p["combine_tokens_not_bit_identical"] == 1
