@@ -32,7 +32,7 @@ def bf16_to_f32(bits):
 
 
 def gate_rel_tol(wl):
-    """Relative gate tolerance derived from fp32 evaluation (see DESIGN.md):
+    """Relative gate tolerance derived from fp32 evaluation:
     softmax: E exponentials (<= 2u each after argument rounding), an E-term
     positive sum and one division; sigmoid-normalised: exp, 1+e, reciprocal,
     a K-term positive sum and one division, plus the reference's rounding."""
