@@ -23,22 +23,26 @@
 extern "C" {
 #endif
 
-/* Reads `bytes` at src with 16-byte non-temporal loads; a fold of the
- * values goes to sink[0] only if it equals a value no input produces, so
- * the loads cannot be dropped.  sink: device uint32 [1]. */
+/* Reads `bytes` at src with 16-byte non-temporal loads, one workgroup per
+ * 16 KiB (4 loads per thread); a fold of the values goes to sink[0] only if
+ * it equals a value no input produces, so the loads cannot be dropped.
+ * sink: device uint32 [1].  The plain streams use short-lived workgroups
+ * started in address order, the fastest pattern measured on MI355X. */
 int32_t moedc_ceiling_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t stream);
 
-/* Writes `bytes` at dst with 16-byte non-temporal stores. */
+/* Writes `bytes` at dst with 16-byte ordinary stores, one workgroup per
+ * 4 KiB. */
 int32_t moedc_ceiling_write(void *dst, int64_t bytes, hipStream_t stream);
 
-/* Copies `bytes` from src to dst with 16-byte non-temporal loads and stores. */
+/* Copies `bytes` from src to dst with 16-byte non-temporal loads and
+ * stores, one workgroup per 4 KiB. */
 int32_t moedc_ceiling_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
 
 /* Dispatch's store pattern without its loads or arithmetic: for each of T
  * tokens, a workgroup writes bytes [0, row_bytes) of each of the token's K
  * slots (slots: device int32 [T][K], -1 skipped) at slot * slot_stride in
- * dbuf, one wave per 512 bytes, 8 bytes per lane per store, non-temporal
- * -- the stores of moedc_dispatch.  row_bytes: a multiple of 8, at most
+ * dbuf, one wave per 512 bytes, 8 bytes per lane per store, ordinary
+ * (cached) stores -- the payload stores of moedc_dispatch.  row_bytes: a multiple of 8, at most
  * 8192. */
 int32_t moedc_ceiling_scatter(const int32_t *slots, int32_t T, int32_t K, void *dbuf,
                               int64_t slot_stride, int32_t row_bytes, hipStream_t stream);
