@@ -1124,7 +1124,7 @@ def summarize_rocprof(d, out):
 # combine on BF16 expert outputs, dispatch with a workgroup per token, the
 # route's top-k kernel and the expert layer's GEMM.
 TRAFFIC_TAGS = {"combine": r"combine_kernel<\d+, false,", "dispatch": r"dispatch_token_block<false>",
-                "route": r"route_topk<", "expert_gemm": r"expert_gemm<true>\("}
+                "route": r"route_topk<", "expert_gemm": r"expert_gemm_groups\("}
 
 
 def record_traffic(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):

@@ -33,14 +33,16 @@
 // rows (tokens), so each lane ends up with 4 consecutive channels of one
 // token (8-byte BF16 stores).  K advances 128 inputs per step; slot rows and
 // weight rows are shared by 4 and 2 waves respectively and pass through a
-// double-buffered LDS tile, loaded one step ahead into registers, with one
-// barrier per step.  With 128-input groups a tile is 128 slot rows x 256
-// channels (waves of 64 x 64) and moves 48 KiB per step for 8.4 MOP
-// (175 op/B).  With one scale per token the int32 sums span the whole row
-// and are scaled once in the epilogue, so the registers that would hold
-// fp32 partial sums hold a second 64 tokens instead: 256 x 256 tiles (waves
-// of 128 tokens x 64 channels), 64 KiB per step for 16.8 MOP (262 op/B),
-// a quarter fewer LDS reads per MFMA and half the tiles and barriers.
+// double-buffered LDS tile, loaded one step ahead into registers.  With
+// 128-input groups a tile is 128 slot rows x 256 channels (waves of 64 x
+// 64), moves 48 KiB per step for 8.4 MOP (175 op/B), and all eight waves
+// meet at one barrier per step.  With one scale per token the int32 sums
+// span the whole row and are scaled once in the epilogue, so the registers
+// that would hold fp32 partial sums hold a second 64 tokens instead: 256 x
+// 256 tiles (waves of 128 tokens x 64 channels), 64 KiB per step for 16.8
+// MOP (262 op/B), a quarter fewer LDS reads per MFMA and half the tiles;
+// there the two halves of the workgroup take turns between MFMAs and
+// staging (see expert_gemm_pt).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -201,25 +203,24 @@ __global__ __launch_bounds__(1024) void gemm_tiles(GemmArgs a) {
 
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
 
-// One K step of the tile, as loaded by one thread: XR x 16 B of slot rows
-// (rows r, r+64, ...; XR = tile rows / 64), 4 x 16 B of weight rows (r,
-// r+64, r+128, r+192) and, at the first step of a scale group, one
-// activation scale (threads below the tile rows).  Rows past the expert's
-// tokens or past H channels read as zero.
-template <int XR>
+// ======== 128-input scale groups: 128 x 256 tiles, one barrier per step ========
+
+// One K step of the tile, as loaded by one thread: 2 x 16 B of slot rows
+// (rows r, r+64), 4 x 16 B of weight rows (r, r+64, r+128, r+192) and the
+// step's activation scale of slot row `tid` (threads below 128).  Rows past
+// the expert's tokens or past H channels read as zero.
 struct StepRegs {
-  v4i x[XR], w[4];
+  v4i x[2], w[4];
   float s;
 };
 
-template <int XR>
-__device__ __forceinline__ StepRegs<XR> fetch_step(const GemmArgs &a, const int8_t *wtile,
-                                                   int64_t slot0, int rows, int chans, int g,
-                                                   int spg, int tid) {
+__device__ __forceinline__ StepRegs fetch_step(const GemmArgs &a, const int8_t *wtile,
+                                               int64_t slot0, int rows, int chans, int g,
+                                               int tid) {
   const int r = tid >> 3, c = 16 * (tid & 7);
-  StepRegs<XR> st;
+  StepRegs st;
 #pragma unroll
-  for (int i = 0; i < XR; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int t = r + 64 * i;
     st.x[i] = t < rows ? ld16(a.dbuf + (slot0 + t) * a.slot_stride + g * BK + c)
                        : v4i{0, 0, 0, 0};
@@ -230,38 +231,32 @@ __device__ __forceinline__ StepRegs<XR> fetch_step(const GemmArgs &a, const int8
     st.w[i] = n < chans ? ld16(wtile + (int64_t)n * a.H + g * BK + c) : v4i{0, 0, 0, 0};
   }
   st.s = 0.0f;
-  if (tid < 64 * XR && g % spg == 0 && tid < rows)
-    st.s = *reinterpret_cast<const float *>(a.dbuf + (slot0 + tid) * a.slot_stride + a.H +
-                                            4 * (g / spg));
+  if (tid < BM && tid < rows)
+    st.s = *reinterpret_cast<const float *>(a.dbuf + (slot0 + tid) * a.slot_stride + a.H + 4 * g);
   return st;
 }
 
-// Scales are double-buffered by group parity: group j's scale is written
-// with its first step and read after its last, while group j+1's goes to
-// the other buffer.
-template <int XR>
-__device__ __forceinline__ void stage(int8_t (&Xs)[64 * XR][BK], int8_t (&Ws)[BN][BK],
-                                      float (&sx)[2][64 * XR], const StepRegs<XR> &st, int g,
-                                      int spg, int tid) {
+// Scales are double-buffered by step parity: step g's scales are written
+// with its slot rows and read after its MFMAs (or, by the lagging waves,
+// after the next barrier), while step g+1's go to the other buffer.
+__device__ __forceinline__ void stage(int8_t (&Xs)[BM][BK], int8_t (&Ws)[BN][BK],
+                                      float (&sx)[2][BM], const StepRegs &st, int g, int tid) {
   const int r = tid >> 3, c = tid & 7;  // rows r + 64 i keep r's low 3 bits
 #pragma unroll
-  for (int i = 0; i < XR; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][swz(r, c)]) = st.x[i];
+  for (int i = 0; i < 2; ++i) *reinterpret_cast<v4i *>(&Xs[r + 64 * i][swz(r, c)]) = st.x[i];
 #pragma unroll
   for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i *>(&Ws[r + 64 * i][swz(r, c)]) = st.w[i];
-  if (tid < 64 * XR && g % spg == 0) sx[(g / spg) & 1][tid] = st.s;
+  if (tid < BM) sx[g & 1][tid] = st.s;
 }
 
-// G128: every K step is one 128-input scale group, so the first MFMA of a
-// step starts from a zero accumulator and the group's int32 sums are folded
-// into fp32 at the end of the same step.  Otherwise one scale spans the row.
-template <bool G128>
-__global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
-  constexpr int TB = G128 ? BM : BM_PT;  // tile rows
-  constexpr int TF = TB / 32;            // 16-token blocks per wave
-  constexpr int XR = TB / 64;            // slot-row loads per thread and step
-  __shared__ __attribute__((aligned(16))) int8_t Xs[2][TB][BK];
+// Every K step is one 128-input scale group: the first MFMA of a step
+// starts from a zero accumulator and the group's int32 sums are folded into
+// fp32 at the end of the step.
+__global__ __launch_bounds__(kThreads) void expert_gemm_groups(GemmArgs a) {
+  constexpr int TF = BM / 32;  // 16-token blocks per wave (4)
+  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BM][BK];
   __shared__ __attribute__((aligned(16))) int8_t Ws[2][BN][BK];
-  __shared__ float sx[2][TB];
+  __shared__ float sx[2][BM];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -269,7 +264,6 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
   const int wm = wave & 1, wn = wave >> 1;  // token half, channel quarter
   const int H = a.H;
   const int ksteps = H / BK;
-  const int spg = G128 ? 1 : a.steps_per_group;  // K steps per activation scale
   const int xcd = blockIdx.x % kXcds;
   const int nblk = gridDim.x / kXcds;  // workgroups sharing this XCD's stream
   const int32_t *row = a.band_pre + xcd * (a.Jmax + 1);
@@ -289,36 +283,31 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
     const int w = min(kBandTiles, a.ntiles - band * kBandTiles);
     const int mt = off / w, nt = band * kBandTiles + off % w;
     const int used = min(a.counts[p], a.cap[p]);
-    const int rows = min(TB, used - mt * TB);
+    const int rows = min(BM, used - mt * BM);
     const int chans = min(BN, H - nt * BN);
-    const int64_t slot0 = (int64_t)a.capbase[p] + (int64_t)mt * TB;
+    const int64_t slot0 = (int64_t)a.capbase[p] + (int64_t)mt * BM;
     const int8_t *wtile = a.W + ((int64_t)p * H + (int64_t)nt * BN) * H;
 
-    // With one scale per token the int32 sums span the whole row and are
-    // scaled once in the epilogue; fp32 accumulators exist only for groups.
     v4i acc[4][TF];
-    float accf[4][G128 ? TF : 1][4];
+    float accf[4][TF][4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
       for (int tf = 0; tf < TF; ++tf) {
         acc[nf][tf] = v4i{0, 0, 0, 0};
-        if (G128) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) accf[nf][tf][q] = 0.0f;
-        }
+        for (int q2 = 0; q2 < 4; ++q2) accf[nf][tf][q2] = 0.0f;
       }
 
     __syncthreads();  // the previous tile's last reads of the LDS tiles are done
-    stage<XR>(Xs[0], Ws[0], sx, fetch_step<XR>(a, wtile, slot0, rows, chans, 0, spg, tid), 0, spg,
-              tid);
-    StepRegs<XR> nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, min(1, ksteps - 1), spg, tid);
+    stage(Xs[0], Ws[0], sx, fetch_step(a, wtile, slot0, rows, chans, 0, tid), 0, tid);
+    StepRegs nxt = fetch_step(a, wtile, slot0, rows, chans, min(1, ksteps - 1), tid);
 
     // Waves 4-7 (the second wave on each SIMD) fold a step's group sums
     // after the next barrier, while waves 0-3 run that step's MFMAs, and run
     // their own MFMAs while waves 0-3 fold: the matrix and vector units of a
     // SIMD stay busy together instead of taking turns.
-    const bool lag = G128 && wave >= 4;
+    const bool lag = wave >= 4;
     for (int g = 0; g < ksteps; ++g) {
       const int buf = g & 1;
       float sv[4];
@@ -327,26 +316,216 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
         for (int tf = 0; tf < 4; ++tf) sv[tf] = sx[(g - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
       }
       __syncthreads();  // step g staged by all; step g-1's reads of buf^1 done
-      if (G128 && lag && g > 0) {
+      if (lag && g > 0) {
 #pragma unroll
         for (int tf = 0; tf < 4; ++tf)
 #pragma unroll
           for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              accf[nf][tf][q] = __builtin_fmaf(sv[tf], (float)acc[nf][tf][q], accf[nf][tf][q]);
+            for (int q2 = 0; q2 < 4; ++q2)
+              accf[nf][tf][q2] = __builtin_fmaf(sv[tf], (float)acc[nf][tf][q2], accf[nf][tf][q2]);
       }
       // Stage step g+1 into the other buffer (free since this barrier) and
-      // issue step g+2's loads: before this step's MFMAs with 128-input
-      // groups, which gives the loads a whole step of lead (1.5% faster),
-      // after them with one scale per token (as fast or faster there).
-      if (G128) {
-        if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
-        if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
-      }
+      // issue step g+2's loads before this step's MFMAs, which gives the
+      // loads a whole step of lead (1.5% faster than after them).
+      if (g + 1 < ksteps) stage(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, tid);
+      if (g + 2 < ksteps) nxt = fetch_step(a, wtile, slot0, rows, chans, g + 2, tid);
       // Raised wave priority while a wave issues its MFMAs, so the SIMD's
-      // other wave (staging, loads, folds) does not delay them (2% faster
-      // with one scale per token, neutral with groups).
+      // other wave (staging, loads, folds) does not delay them.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        v4i av[4], bv[4];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+          av[nf] = *reinterpret_cast<const v4i *>(
+              &Ws[buf][64 * wn + 16 * nf + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bv[i] = *reinterpret_cast<const v4i *>(
+              &Xs[buf][16 * TF * wm + 16 * i + (lane & 15)][swz(lane, 4 * kk + (lane >> 4))]);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nf][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                av[nf], bv[i], kk == 0 ? v4i{0, 0, 0, 0} : acc[nf][i], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (!lag) {  // end of the step's scale group
+#pragma unroll
+        for (int tf = 0; tf < 4; ++tf) {
+          const float sc = sx[g & 1][64 * wm + 16 * tf + (lane & 15)];
+#pragma unroll
+          for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+              accf[nf][tf][q2] = __builtin_fmaf(sc, (float)acc[nf][tf][q2], accf[nf][tf][q2]);
+        }
+      }
+    }
+    if (lag) {  // the last step's fold (its scales are not restaged before the next tile)
+#pragma unroll
+      for (int tf = 0; tf < 4; ++tf) {
+        const float sc = sx[(ksteps - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2)
+            accf[nf][tf][q2] = __builtin_fmaf(sc, (float)acc[nf][tf][q2], accf[nf][tf][q2]);
+      }
+    }
+
+    // ---- epilogue: lane holds channels n0..n0+3 of token 64 wm + 16 tf + lane%16 ----
+    // Token rows one after another: the four 32-byte stores that make up a
+    // row's 128-byte line issue back to back and the line reaches memory
+    // whole (channel-major order left lines partly written in L2: up to
+    // 1.85x the output bytes written).  Weight scales load at each store
+    // (loaded once per tile they cost two more spilled registers, +3.5%).
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) {
+      const int t = 16 * TF * wm + 16 * tf + (lane & 15);
+      if (t >= rows) continue;
+#pragma unroll
+      for (int nf = 0; nf < 4; ++nf) {
+        const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
+        if (nl >= chans) continue;
+        const int64_t n0 = (int64_t)nt * BN + nl;
+        const float4 w4 = *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H + n0);
+        const uint2 o = make_uint2(pack_bf16x2(accf[nf][tf][0] * w4.x, accf[nf][tf][1] * w4.y),
+                                   pack_bf16x2(accf[nf][tf][2] * w4.z, accf[nf][tf][3] * w4.w));
+        *reinterpret_cast<uint2 *>(a.ebuf + (slot0 + t) * (int64_t)H + n0) = o;
+      }
+    }
+  }
+}
+
+// ======== one scale per token: 256 x 256 tiles, two wave groups in turn ========
+//
+// Waves 0-3 (group A: output channels 0-127) and 4-7 (group B: channels
+// 128-255) alternate between a compute phase (a step's 64 MFMAs per wave,
+// from LDS fragments) and a memory phase (staging the group's half of a
+// later step into LDS and issuing the global loads of the one after), with
+// a workgroup barrier between phases; group B starts one phase late, so on
+// every SIMD one wave issues MFMAs while the other stages.  Group A stages
+// slot rows 0-127 and weight rows 0-127, group B rows 128-255 of both.  A
+// computes on step g, then stages step g + 1; B computes on step g, then
+// stages step g + 2: every step is complete one phase before either group
+// computes on it, and two LDS buffers suffice (a buffer is rewritten only
+// after both groups have computed on the step it held).  Against one
+// barrier per step with all eight waves in the same phase (the 128-input
+// kernel's scheme): 12.1-12.4 ms against 13.3-13.6 ms on the 30720-token
+// batch, bit-identical.
+
+// Slot rows 128 grp + r + 32 i and weight rows likewise (r = gt / 8, the
+// thread's index in its group over 8), 16-byte column gt % 8 of the step's
+// 128 inputs; the loads address a uniform base plus a 32-bit lane offset.
+struct PartRegs {
+  v4i x[4], w[4];
+  float s;
+};
+
+__device__ __forceinline__ PartRegs fetch_part(const int8_t *xb, const int8_t *wb, uint32_t xo,
+                                               uint32_t wo, uint32_t xstep, uint32_t wstep,
+                                               int rows, int chans, int g, int grp, int gt,
+                                               const int8_t *sb) {
+  const int r = gt >> 3;
+  PartRegs st;
+  const int8_t *xg = xb + g * BK;
+  const int8_t *wg = wb + g * BK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 128 * grp + r + 32 * i;
+    st.x[i] = t < rows ? ld16(xg + (xo + i * xstep)) : v4i{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = 128 * grp + r + 32 * i;
+    st.w[i] = n < chans ? ld16(wg + (wo + i * wstep)) : v4i{0, 0, 0, 0};
+  }
+  // The token's scale, with the first step (slot rows 128 grp + gt, gt < 128).
+  st.s = 0.0f;
+  if (g == 0 && gt < 128 && 128 * grp + gt < rows) st.s = *reinterpret_cast<const float *>(sb);
+  return st;
+}
+
+__device__ __forceinline__ void stage_part(int8_t (&Xs)[BM_PT][BK], int8_t (&Ws)[BN][BK],
+                                           float (&sx)[BM_PT], const PartRegs &st, int g,
+                                           int grp, int gt) {
+  const int r = gt >> 3, c = gt & 7;  // rows 128 grp + r + 32 i keep r's low 3 bits
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<v4i *>(&Xs[128 * grp + r + 32 * i][swz(r, c)]) = st.x[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<v4i *>(&Ws[128 * grp + r + 32 * i][swz(r, c)]) = st.w[i];
+  if (g == 0 && gt < 128) sx[128 * grp + gt] = st.s;
+}
+
+__global__ __launch_bounds__(kThreads) void expert_gemm_pt(GemmArgs a) {
+  constexpr int TF = BM_PT / 32;  // 16-token blocks per wave (8)
+  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BM_PT][BK];
+  __shared__ __attribute__((aligned(16))) int8_t Ws[2][BN][BK];
+  __shared__ float sx[BM_PT];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = uniform(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // token half, channel quarter
+  const int grp = wave >> 2;                // 0: channels 0-127, 1: channels 128-255
+  const int gt = tid & 255;                 // thread index within the group
+  const int H = a.H;
+  const int ksteps = H / BK;
+  const int xcd = blockIdx.x % kXcds;
+  const int nblk = gridDim.x / kXcds;
+  const int32_t *row = a.band_pre + xcd * (a.Jmax + 1);
+  const int J = uniform(a.band_cnt[xcd]);
+  const int total = uniform(row[J]);
+
+  for (int q = blockIdx.x / kXcds; q < total; q += nblk) {
+    int lo = 0, hi = J;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (row[mid] <= q) lo = mid; else hi = mid;
+    }
+    const int k = uniform(a.band_list[xcd * a.Jmax + lo]);
+    const int p = k / a.nbe, band = k % a.nbe;
+    const int off = q - row[lo];
+    const int w = min(kBandTiles, a.ntiles - band * kBandTiles);
+    const int mt = off / w, nt = band * kBandTiles + off % w;
+    const int used = min(a.counts[p], a.cap[p]);
+    const int rows = min(BM_PT, used - mt * BM_PT);
+    const int chans = min(BN, H - nt * BN);
+    const int64_t slot0 = (int64_t)a.capbase[p] + (int64_t)mt * BM_PT;
+    const int8_t *wtile = a.W + ((int64_t)p * H + (int64_t)nt * BN) * H;
+    const int8_t *xb = reinterpret_cast<const int8_t *>(a.dbuf) + slot0 * a.slot_stride;
+    const uint32_t xstep = 32u * (uint32_t)a.slot_stride, wstep = 32u * (uint32_t)H;
+    const uint32_t xo = (uint32_t)(128 * grp + (gt >> 3)) * (uint32_t)a.slot_stride + 16u * (gt & 7);
+    const uint32_t wo = (uint32_t)(128 * grp + (gt >> 3)) * (uint32_t)H + 16u * (gt & 7);
+    const int8_t *sb = xb + (int64_t)(128 * grp + gt) * a.slot_stride + H;
+    auto fetch = [&](int g) {
+      return fetch_part(xb, wtile, xo, wo, xstep, wstep, rows, chans, g, grp, gt, sb);
+    };
+
+    v4i acc[4][TF];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+      for (int tf = 0; tf < TF; ++tf) acc[nf][tf] = v4i{0, 0, 0, 0};
+
+    __syncthreads();  // the previous tile's reads of the LDS tiles and scales are done
+    stage_part(Xs[0], Ws[0], sx, fetch(0), 0, grp, gt);
+    if (grp == 1 && ksteps > 1) stage_part(Xs[1], Ws[1], sx, fetch(1), 1, grp, gt);
+    // The step this group stages next (A: 1, B: 2) is loaded ahead.
+    PartRegs nxt;
+    const int first = 1 + grp;
+    if (first < ksteps) nxt = fetch(first);
+    __syncthreads();                // step 0 (and B's half of step 1) staged
+    if (grp == 1) __syncthreads();  // group B runs one phase behind group A
+
+    for (int g = 0; g < ksteps; ++g) {
+      const int buf = g & 1;
+      // ---- compute phase, at raised wave priority ----
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -367,79 +546,48 @@ __global__ __launch_bounds__(kThreads) void expert_gemm(GemmArgs a) {
           for (int nf = 0; nf < 4; ++nf)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[nf][t0 + i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                  av[nf], bv[i], (G128 && kk == 0) ? v4i{0, 0, 0, 0} : acc[nf][t0 + i], 0, 0, 0);
+              acc[nf][t0 + i] =
+                  __builtin_amdgcn_mfma_i32_16x16x64_i8(av[nf], bv[i], acc[nf][t0 + i], 0, 0, 0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      if (!G128) {
-        if (g + 1 < ksteps) stage<XR>(Xs[buf ^ 1], Ws[buf ^ 1], sx, nxt, g + 1, spg, tid);
-        if (g + 2 < ksteps) nxt = fetch_step<XR>(a, wtile, slot0, rows, chans, g + 2, spg, tid);
+      __syncthreads();
+      // ---- memory phase: stage step st_g, load step st_g + 1 ----
+      const int st_g = g + 1 + grp;
+      if (st_g < ksteps) {
+        stage_part(Xs[st_g & 1], Ws[st_g & 1], sx, nxt, st_g, grp, gt);
+        if (st_g + 1 < ksteps) nxt = fetch(st_g + 1);
       }
-
-      if (G128 && !lag) {  // end of the step's scale group
-#pragma unroll
-        for (int tf = 0; tf < 4; ++tf) {
-          const float s = sx[g & 1][64 * wm + 16 * tf + (lane & 15)];
-#pragma unroll
-          for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              accf[nf][tf][q] = __builtin_fmaf(s, (float)acc[nf][tf][q], accf[nf][tf][q]);
-        }
-      }
-    }
-    if (G128 && lag) {  // the last step's fold (its scales are not restaged before the next tile)
-#pragma unroll
-      for (int tf = 0; tf < 4; ++tf) {
-        const float s = sx[(ksteps - 1) & 1][64 * wm + 16 * tf + (lane & 15)];
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            accf[nf][tf][q] = __builtin_fmaf(s, (float)acc[nf][tf][q], accf[nf][tf][q]);
-      }
+      // Group B's last memory phase has nothing to do and no partner phase.
+      if (grp == 0 || g + 1 < ksteps) __syncthreads();
     }
 
-    // ---- epilogue: lane holds channels n0..n0+3 of token 16 TF wm + 16 tf + lane%16 ----
-    // Token rows one after another: the four 32-byte stores that make up a
-    // row's 128-byte line issue back to back and the line reaches memory
-    // whole (channel-major order left lines partly written in L2: up to
-    // 1.85x the output bytes written).  Weight scales load at each store
-    // with 128-input groups and once per tile with one scale per token (the
-    // register allocation that ran faster for each).
+    // ---- epilogue: lane holds channels n0..n0+3 of token 128 wm + 16 tf + lane%16 ----
+    // The one group's fold, fma(s, isum, +0), then the weight scale; token
+    // rows one after another, as above.
     float4 ws[4];
-    if (!G128) {
 #pragma unroll
-      for (int nf = 0; nf < 4; ++nf) {
-        const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
-        ws[nf] = nl < chans ? *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H +
-                                                                 nt * BN + nl)
-                            : float4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+    for (int nf = 0; nf < 4; ++nf) {
+      const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
+      ws[nf] = nl < chans ? *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H +
+                                                               nt * BN + nl)
+                          : float4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) {
       const int t = 16 * TF * wm + 16 * tf + (lane & 15);
       if (t >= rows) continue;
-      const float s = G128 ? 0.0f : sx[0][t];
+      const float sc = sx[t];
 #pragma unroll
       for (int nf = 0; nf < 4; ++nf) {
         const int nl = 64 * wn + 16 * nf + 4 * (lane >> 4);
         if (nl >= chans) continue;
         const int64_t n0 = (int64_t)nt * BN + nl;
-        const float4 w4 =
-            G128 ? *reinterpret_cast<const float4 *>(a.w_scale + (int64_t)p * H + n0) : ws[nf];
         float v[4];
-        if (G128) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = accf[nf][G128 ? tf : 0][q];
-        } else {  // the one group's fold: fma(s, isum, +0)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(s, (float)acc[nf][tf][q], 0.0f);
-        }
-        const uint2 o = make_uint2(pack_bf16x2(v[0] * w4.x, v[1] * w4.y),
-                                   pack_bf16x2(v[2] * w4.z, v[3] * w4.w));
+        for (int q2 = 0; q2 < 4; ++q2) v[q2] = __builtin_fmaf(sc, (float)acc[nf][tf][q2], 0.0f);
+        const uint2 o = make_uint2(pack_bf16x2(v[0] * ws[nf].x, v[1] * ws[nf].y),
+                                   pack_bf16x2(v[2] * ws[nf].z, v[3] * ws[nf].w));
         *reinterpret_cast<uint2 *>(a.ebuf + (slot0 + t) * (int64_t)H + n0) = o;
       }
     }
@@ -456,9 +604,9 @@ hipError_t launch_expert_gemm(const GemmArgs &args, int grid, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.steps_per_group == 1)
-    expert_gemm<true><<<grid, kThreads, 0, s>>>(a);
+    expert_gemm_groups<<<grid, kThreads, 0, s>>>(a);
   else
-    expert_gemm<false><<<grid, kThreads, 0, s>>>(a);
+    expert_gemm_pt<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

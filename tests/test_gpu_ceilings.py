@@ -23,7 +23,7 @@ def _stream():
 
 def test_write_and_copy_streams_cover_every_byte():
     L = _lib()
-    n = 3 << 20                                     # not a multiple of the grid stride
+    n = (3 << 20) + 48                              # not a multiple of a workgroup's 4 or 16 KiB
     a = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
     b = torch.zeros(n, dtype=torch.uint8, device="cuda")
     assert L.moedc_ceiling_copy(b.data_ptr(), a.data_ptr(), n, _stream()) == 0
