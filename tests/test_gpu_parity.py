@@ -616,8 +616,11 @@ def test_expert_w8a8_parity(name):
 
 # 150 and 70 tokens: one partial tile per expert; 1500 and 1300 tokens:
 # experts of ~560 and ~490 rows span two or three 256-row tiles with a
-# ragged last one, and H = 1152 ends in a 128-channel tile.
-@pytest.mark.parametrize("H,T", [(1024, 150), (2048, 70), (1024, 1500), (1152, 1300)])
+# ragged last one, and H = 1152 ends in a 128-channel tile.  H = 384 and
+# 256: three and two K steps (the two wave groups' first and last phases
+# meet), H = 384 with a 128-channel last tile.
+@pytest.mark.parametrize("H,T", [(1024, 150), (2048, 70), (1024, 1500), (1152, 1300),
+                                 (384, 300), (256, 900)])
 def test_expert_w8a8_parity_per_token(H, T):
     wl = W.Workload("pt", "", T, H, 8, 8, 3, 0, W.SCORE_SIGMOID_NORM,
                     np.full(8, T, np.int32), None, 31, "normal", ("fraction", 0.05, 50.0),
