@@ -1123,7 +1123,7 @@ def summarize_rocprof(d, out):
 # Kernel of each path step in a one-workload bench run (name patterns):
 # combine on BF16 expert outputs, dispatch with a workgroup per token, the
 # route's top-k kernel and the expert layer's GEMM.
-TRAFFIC_TAGS = {"combine": r"combine_kernel<\d+, false,", "dispatch": r"dispatch_token_block<false>",
+TRAFFIC_TAGS = {"combine": r"combine_kernel<\d+, false,", "dispatch": r"dispatch_token_block<false, true>",
                 "route": r"route_topk<", "expert_gemm": r"expert_gemm_groups\("}
 
 

@@ -19,12 +19,15 @@
 // writes its chunk's payload (8 bytes per lane, 512 contiguous bytes per
 // store instruction) into each of the token's K slots, and one wave writes
 // the slot's scale region -- the scales, gathered through LDS, then zero
-// words up to a 128-byte boundary -- as whole lines.  Payload stores are
-// ordinary (cached) stores and the scale lines carry the non-temporal hint:
-// on the 30720-token batch the cached payload stores shorten dispatch from
-// 429-431 to 410-411 us in the route -> dispatch -> combine sequence
-// (non-temporal payload stores were the faster choice when one wave walked
-// a whole token); the hint on the scale lines makes no difference.
+// words up to a 128-byte boundary -- as whole lines with the non-temporal
+// hint.  The payload goes through non-temporal stores while the batch's
+// BF16 input fits in the memory-side cache (256 MiB) and through ordinary
+// (cached) stores above that, each the faster one there in the route ->
+// dispatch -> combine sequence at hidden 7168: non-temporal 188 against
+// 224 us at 16384 tokens (cached stores evict the input from that cache),
+// cached 277 against 286 us at 20480 and 411-413 against 430 us at 30720
+// tokens; on decode batches non-temporal 4.1 against 4.3 us at 96 tokens
+// and 4.7 against 5.6 us at 256.
 // A token's K slots are thus written by all its waves at once: 6% faster on
 // a 30720-token batch than one wave walking the token's K x 7 KiB of slots,
 // and 2.2x faster on a 96-token decode batch with one scale per token.
@@ -61,6 +64,18 @@ __device__ int64_t g_trace_records = 0;
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+
+// A lane's 8 payload bytes: ordinary (cached) or non-temporal store.  A
+// compile-time choice: with a run-time branch the compiler merges the two
+// stores of the same value into one ordinary store.
+template <bool CACHED>
+__device__ __forceinline__ void store_payload(const uint2 &q, uint8_t *dst) {
+  const u32x2 qq = {q.x, q.y};
+  if (CACHED)
+    *reinterpret_cast<u32x2 *>(dst) = qq;
+  else
+    __builtin_nontemporal_store(qq, reinterpret_cast<u32x2 *>(dst));
+}
 constexpr int kSplitMaxTokens = 16;
 
 // One wave per (token, 512-value chunk); 128-value groups only.
@@ -86,17 +101,14 @@ __global__ __launch_bounds__(256) void dispatch_split(DispatchArgs a, int nch) {
     const int slot = __builtin_amdgcn_readlane(my_slot, k);
     if ((uint32_t)slot >= (uint32_t)a.total_slots) continue;  // -1: dropped
     uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
-    if (e < H) {
-      const u32x2 qq = {q.x, q.y};
-      *reinterpret_cast<u32x2 *>(dst + e) = qq;
-    }
+    if (e < H) store_payload<false>(q, dst + e);  // at most 16 tokens: always non-temporal
     if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 }
 
 // One workgroup per token, wave c holding chunk c (blockDim = 64 x chunks).
 // wave_max: the waves' maxima (one scale per token) or the groups' scales.
-template <bool PER_TOKEN>
+template <bool PER_TOKEN, bool CACHED>
 __global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
   __shared__ uint32_t wave_max[64];
   __shared__ int slot_of[kMaxK];
@@ -154,10 +166,7 @@ __global__ __launch_bounds__(1024) void dispatch_token_block(DispatchArgs a) {
     const int slot = slot_of[k];
     if (slot < 0) continue;  // dropped, or outside the buffer
     uint8_t *dst = a.dbuf + (int64_t)slot * a.slot_stride;
-    if (e < H) {
-      const u32x2 qq = {q.x, q.y};
-      *reinterpret_cast<u32x2 *>(dst + e) = qq;
-    }
+    if (e < H) store_payload<CACHED>(q, dst + e);
     if (has_word) __builtin_nontemporal_store(word, reinterpret_cast<float *>(dst + H + 4 * lane));
   }
 #ifdef MOEDC_TRACE
@@ -196,9 +205,15 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s) {
     const int64_t units = (int64_t)a.T * nch;
     dispatch_split<<<(unsigned)((units + kWavesPerBlock - 1) / kWavesPerBlock), 256, 0, s>>>(a, nch);
   } else if (a.per_token) {
-    dispatch_token_block<true><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
+    if (a.cached_payload)
+      dispatch_token_block<true, true><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
+    else
+      dispatch_token_block<true, false><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
   } else {
-    dispatch_token_block<false><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
+    if (a.cached_payload)
+      dispatch_token_block<false, true><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
+    else
+      dispatch_token_block<false, false><<<(unsigned)a.T, 64 * nch, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -280,6 +280,7 @@ moedc::DispatchArgs dispatch_args(const moedc_plan *p, int32_t T, const uint16_t
   a.K = p->K;
   a.per_token = p->G == 1;
   a.total_slots = (int32_t)p->total_slots;
+  a.cached_payload = (int64_t)T * 2 * a.H > moedc::kStreamInputBytes;
   return a;
 }
 

@@ -72,7 +72,13 @@ struct DispatchArgs {
   int32_t T, H, G, K;
   int32_t per_token;    // one scale per token (G == 1) instead of per 128 values
   int32_t total_slots;  // entries outside [0, total_slots) are skipped
+  int32_t cached_payload;  // payload through ordinary stores (inputs larger than kStreamInputBytes)
 };
+
+// Dispatch batches whose BF16 input is at most this many bytes (the MI355X
+// memory-side cache's capacity) write their payload with non-temporal
+// stores, larger ones with ordinary ones.
+constexpr int64_t kStreamInputBytes = int64_t(256) << 20;
 
 struct CombineArgs {
   const uint8_t *eout;

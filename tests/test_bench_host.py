@@ -66,7 +66,7 @@ def test_record_traffic_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     comb = "void moedc::(anonymous namespace)::combine_kernel<8, false, 16, 1>(moedc::CombineArgs)"
     comb_q8 = "void moedc::(anonymous namespace)::combine_kernel<8, true, 16, 1>(moedc::CombineArgs)"
-    disp = "void moedc::(anonymous namespace)::dispatch_token_block<false>(moedc::DispatchArgs)"
+    disp = "void moedc::(anonymous namespace)::dispatch_token_block<false, true>(moedc::DispatchArgs)"
     _write_csv(str(tmp_path / "f" / "f_counter_collection.csv"), hdr,
                [[comb, "FETCH_SIZE", 1000.0], [comb, "FETCH_SIZE", 1000.0],
                 [comb_q8, "FETCH_SIZE", 7.0], [disp, "FETCH_SIZE", 300.0]])
@@ -140,7 +140,7 @@ def test_source_hash_covers_every_file_of_a_kernel(tmp_path, monkeypatch):
 
 def test_summary_splits_a_kernel_launched_with_several_grid_sizes(tmp_path):
     """One kernel serving two batch sizes gets one row per launch shape."""
-    name = "void moedc::(anonymous namespace)::dispatch_token_block<false>(moedc::DispatchArgs)"
+    name = "void moedc::(anonymous namespace)::dispatch_token_block<false, true>(moedc::DispatchArgs)"
     _write_csv(str(tmp_path / "p" / "b_kernel_stats.csv"),
                ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
                [[name, 3, 1000.0, 4000.0, 430000.0, 100.0]])
