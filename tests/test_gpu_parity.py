@@ -250,6 +250,36 @@ def test_dispatch_combine_around_split_threshold(T):
     log(f"  dropped {r['dropped']}; dispatch and combine bit-exact")
 
 
+def test_dispatch_store_kinds_agree_at_the_input_size_threshold():
+    """Dispatch writes the payload with non-temporal stores while the batch's
+    BF16 input is at most 256 MiB and with ordinary stores above.  At hidden
+    8192, 16384 tokens are exactly 256 MiB and 16385 tokens one row more:
+    a token's slot depends only on the tokens before it, so both calls must
+    leave identical bytes in every slot but the extra token's, and both
+    agree with the oracle on a sample of tokens (the extra one included)."""
+    T, H, E, K = 16385, 8192, 256, 8
+    cap = np.full(E, 2 * T * K // E, np.int32)
+    wl = W.Workload("thr", "", T, H, E, E, K, 0, W.SCORE_SIGMOID_NORM, cap, None, 77, "normal")
+    log(f"[case] dispatch at the input-size threshold: T={T - 1} and {T}, H={H}")
+    x, logits = W.make_inputs(wl)
+    plan = M.Plan.from_workload(wl)
+    cfg = oracle.Cfg.from_workload(wl)
+    r = oracle.route(cfg, logits)
+    assert r["dropped"] == 0
+    assert (T - 1) * 2 * H == 256 << 20
+    a = gpu_dispatch(plan, x[:T - 1], r["slots"][:T - 1])      # non-temporal payload stores
+    b = gpu_dispatch(plan, x, r["slots"])                       # ordinary payload stores
+    last = torch.tensor([int(sl) for sl in r["slots"][T - 1] if sl >= 0], device="cuda",
+                        dtype=torch.long)
+    b[last] = SENTINEL
+    assert torch.equal(a, b), "the two store kinds left different bytes"
+    del a
+    b = gpu_dispatch(plan, x, r["slots"])
+    sample = np.concatenate([np.arange(0, T - 1, 997), [T - 1]])
+    check_dispatch_tokens(b, x, r["slots"], sample, H)
+    log(f"  identical slots below the extra token; {sample.size} tokens bit-exact against the oracle")
+
+
 def test_combine_dropped_entries_and_signed_zero():
     rng = np.random.default_rng(91)
     T, H, K, S = 300, 640, 4, 500
